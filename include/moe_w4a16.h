@@ -1,0 +1,161 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) W4A16 routed-expert MoE layer.
+ *
+ * The layer (Kimi-K2.6 inference-research catalog entry, MoE and QUANT
+ * paragraphs; lmdeploy pull request "support Kimi K2.6", Changes list, which
+ * names the compressed-tensors W4A16 MoE kernels):
+ *
+ *   out[t] = bf16( S(x_t) + sum_{j<k, id_tj local} w_tj * F_{id_tj - base}(x_t) )
+ *   F_e(v) = W2_e ( silu(W1_e v) * (W3_e v) ),   W1_e = W13_e[0:I], W3_e = W13_e[I:2I]
+ *   W[n][c] = (u - 8) * s[n][c/32],  u = 4-bit field c%8 (bits 4(c%8)..) of word c/8
+ *   S = the same MLP with the bf16 shared-expert weights, added with weight 1
+ *
+ * Routed experts are symmetric INT4 with one bf16 scale per 32 inputs along
+ * the input dimension, eight codes per int32 word (QUANT and PARAMS
+ * paragraphs); the shared expert is bf16 (QUANT paragraph: kept in higher
+ * precision). Hidden 7168, 384 experts, top-8 and moe_intermediate 2048 are
+ * the catalog's geometry; the library takes any shape meeting the limits
+ * below.
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major, and live in device memory unless marked
+ *    "host". Every device pointer must be 16-byte aligned.
+ *  - The caller allocates and owns every buffer, including the workspace, and
+ *    keeps it alive until the stream work completes. The library allocates
+ *    nothing, keeps no pointer after it returns, never synchronises the host
+ *    and launches only on `stream` (a hipStream_t; NULL is the null stream) on
+ *    the current device. Calls that share a workspace must not overlap.
+ *  - Every argument error is detected on the host before any launch (so a
+ *    failing call writes nothing) and reported as a negative status. Routing
+ *    data on the device is never an error: ids outside [expert_base,
+ *    expert_base + num_experts), -1 included, contribute nothing. NaNs
+ *    propagate.
+ *  - Limits: 1 <= top_k <= 16; 1 <= num_experts <= 512; hidden and inter
+ *    multiples of 128; group_size == 32; num_tokens * top_k < 2^31 - 1.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)       /* a size is out of range */
+#define MOE_ERR_ALIGNMENT (-3)   /* a device pointer is not 16-byte aligned */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace or output buffer too small */
+#define MOE_ERR_UNSUPPORTED (-5) /* a valid but unsupported configuration */
+#define MOE_ERR_HIP (-6)         /* a HIP call failed; see moe_w4a16_status_string */
+
+#define MOE_MAX_TOP_K 16
+#define MOE_MAX_EXPERTS 512
+
+/* Problem sizes (host struct, read during the call only). */
+typedef struct {
+  int64_t num_tokens; /* T >= 0; T == 0 is a successful no-op */
+  int32_t hidden;     /* H: input and output width, multiple of 128 */
+  int32_t inter;      /* I: expert intermediate width, multiple of 128 */
+  int32_t num_experts;/* E: experts present in packed_w13 / packed_w2 */
+  int32_t expert_base;/* global id of local expert 0 (expert parallelism) */
+  int32_t top_k;      /* k: routing slots per token */
+  int32_t group_size; /* quantisation group along the input dim, must be 32 */
+} moe_w4a16_problem;
+
+/*
+ * Bytes of device workspace moe_w4a16_forward needs for `p` (host-only, no
+ * GPU call). Writes *bytes (host). Returns a status.
+ */
+int moe_w4a16_workspace_size(const moe_w4a16_problem *p, size_t *bytes);
+
+/*
+ * The bucket granularity (rows per GEMM block) moe_w4a16_forward uses for
+ * `p`. Writes *block_m (host). Returns a status.
+ */
+int moe_w4a16_forward_block_m(const moe_w4a16_problem *p, int32_t *block_m);
+
+/*
+ * Capacities moe_w4a16_align needs: *sorted_capacity int32 entries for
+ * sorted_ids and *block_capacity entries for block_expert (both host out).
+ * sorted_capacity = T*k + min(E, T*k) * (block_m - 1), the largest possible
+ * padded count; block_capacity = sorted_capacity / block_m.
+ */
+int moe_w4a16_align_capacity(const moe_w4a16_problem *p, int32_t block_m,
+                             int64_t *sorted_capacity, int64_t *block_capacity);
+
+/*
+ * Token/expert bucketing used by the grouped GEMMs (exported so it can be
+ * checked bit for bit). The pages name the grouped W4A16 MoE kernels without
+ * their internals; the ordering defined here is the one this library uses.
+ *
+ *   topk_ids     int32 [T, k] (device)
+ *   sorted_ids   int32 [sorted_capacity] (device, out): the valid pairs
+ *                p = t*k + j of local expert 0 in ascending p, padded with the
+ *                sentinel T*k to a multiple of block_m, then expert 1, ...;
+ *                experts without pairs take no space. Entries at and past
+ *                n_padded are left unspecified.
+ *   block_expert int32 [block_capacity] (device, out): local expert of each
+ *                block of block_m entries of sorted_ids.
+ *   n_padded     int32 [1] (device, out): number of meaningful sorted_ids.
+ *
+ * 1 <= block_m <= 1024. Returns MOE_ERR_WORKSPACE if a capacity is below the
+ * value moe_w4a16_align_capacity reports.
+ */
+int moe_w4a16_align(const int32_t *topk_ids, const moe_w4a16_problem *p, int32_t block_m,
+                    int32_t *sorted_ids, int64_t sorted_capacity, int32_t *block_expert,
+                    int64_t block_capacity, int32_t *n_padded, void *stream);
+
+/*
+ * The layer.
+ *
+ *   x            bf16  [T, H]
+ *   topk_ids     int32 [T, k]   global expert ids; local expert = id - expert_base
+ *   topk_weights fp32  [T, k]   applied as given (no renormalisation)
+ *   packed_w13   int32 [E, 2I, H/8]  rows 0..I-1 gate, rows I..2I-1 up
+ *   scales_w13   bf16  [E, 2I, H/32]
+ *   packed_w2    int32 [E, H, I/8]
+ *   scales_w2    bf16  [E, H, I/32]
+ *   shared_w     bf16  [2I*H + H*I] (gate/up [2I, H], then down [H, I]) or NULL
+ *   out          bf16  [T, H], fully overwritten; must not alias an input
+ *   workspace    device scratch of at least moe_w4a16_workspace_size bytes
+ *
+ * Numerics: bf16 x bf16 matrix products with fp32 accumulation; the
+ * dequantised weights and the SwiGLU output h are rounded to bf16 before
+ * their products, everything else stays fp32 until the final bf16 rounding
+ * (round to nearest even).
+ */
+int moe_w4a16_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                      const int32_t *packed_w13, const void *scales_w13,
+                      const int32_t *packed_w2, const void *scales_w2, const void *shared_w,
+                      void *out, const moe_w4a16_problem *p, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * moe_w4a16_forward with stage timing: identical work and results, and in
+ * addition records the caller's HIP events (hipEvent_t, created by the caller;
+ * NULL entries are skipped) on `stream`: stage_events[0] before the bucketing,
+ * [1] before the gate_up GEMM, [2] before the down GEMM, [3] before the
+ * combine and [4] after it. Used to time each kernel on its own stream.
+ */
+int moe_w4a16_forward_timed(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                            const int32_t *packed_w13, const void *scales_w13,
+                            const int32_t *packed_w2, const void *scales_w2,
+                            const void *shared_w, void *out, const moe_w4a16_problem *p,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            void *const *stage_events);
+
+/*
+ * A static description of `status`; for MOE_ERR_HIP it names the HIP error
+ * of the failing call on this thread. Never NULL.
+ */
+const char *moe_w4a16_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

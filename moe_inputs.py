@@ -97,19 +97,29 @@ TINY = Geometry(hidden=256, inter=128, n_experts=8, top_k=2, shared=False)
 # --------------------------------------------------------------------------
 # weights
 # --------------------------------------------------------------------------
+def _uniform_f32(rng: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
+    return rng.random(size=shape, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)
+
+
 def _scales(rng: np.random.Generator, rows: int, groups: int) -> np.ndarray:
-    s = rng.uniform(SCALE_LO, SCALE_HI, size=(rows, groups)).astype(np.float32)
-    return f32_to_bf16_bits(s)
+    return f32_to_bf16_bits(_uniform_f32(rng, (rows, groups), SCALE_LO, SCALE_HI))
+
+
+def _random_words(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform random 32-bit words (two per 64-bit output of the generator)."""
+    n = int(np.prod(shape))
+    raw = rng.bit_generator.random_raw((n + 1) // 2)
+    return raw.view("<i4")[:n].reshape(shape)
 
 
 def expert_weights(seed: int, e: int, hidden: int, inter: int):
     """One routed expert: (packed_w13 [2I, H/8], scales_w13 [2I, H/32],
     packed_w2 [H, I/8], scales_w2 [H, I/32])."""
     r13 = _rng(seed, TAG_W13, e)
-    pw13 = r13.integers(0, 1 << 32, size=(2 * inter, hidden // 8), dtype=np.uint32).view(np.int32)
+    pw13 = _random_words(r13, (2 * inter, hidden // 8))
     s13 = _scales(r13, 2 * inter, hidden // GROUP)
     r2 = _rng(seed, TAG_W2, e)
-    pw2 = r2.integers(0, 1 << 32, size=(hidden, inter // 8), dtype=np.uint32).view(np.int32)
+    pw2 = _random_words(r2, (hidden, inter // 8))
     s2 = _scales(r2, hidden, inter // GROUP)
     return pw13, s13, pw2, s2
 
@@ -144,9 +154,10 @@ def shared_weights(seed: int, hidden: int, inter: int) -> np.ndarray:
     r = _rng(seed, TAG_SHARED)
 
     def mat(rows: int, cols: int) -> np.ndarray:
-        q = r.integers(-8, 8, size=(rows, cols)).astype(np.float32)
-        s = r.uniform(SCALE_LO, SCALE_HI, size=(rows, cols // GROUP)).astype(np.float32)
-        return f32_to_bf16_bits(q * np.repeat(s, GROUP, axis=1))
+        q = (_random_words(r, (rows * cols + 3) // 4).view(np.uint8)[:rows * cols] & 15).astype(np.float32) - 8.0
+        s = _uniform_f32(r, (rows, cols // GROUP), SCALE_LO, SCALE_HI)
+        w = q.reshape(rows, cols // GROUP, GROUP) * s[:, :, None]
+        return f32_to_bf16_bits(w.reshape(rows, cols))
 
     return np.concatenate([mat(2 * inter, hidden).ravel(), mat(hidden, inter).ravel()])
 
@@ -258,3 +269,52 @@ def make_inputs(w: Workload, bank: Optional[Bank] = None):
     shared = shared_weights(w.seed_bank, g.hidden, g.inter) if g.shared else None
     return dict(x=x, topk_ids=ids, topk_weights=wts, bank=bank, shared_w=shared,
                 expert_base=w.expert_base)
+
+
+# --------------------------------------------------------------------------
+# host <-> device (uint16 arrays are bf16 bit patterns)
+# --------------------------------------------------------------------------
+def to_device(a: np.ndarray, device):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def bf16_tensor_to_f64(t) -> np.ndarray:
+    import torch
+
+    b = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def device_bank(seed: int, hidden: int, inter: int, experts: Sequence[int], device) -> dict:
+    """The bank of `experts` generated expert by expert straight into device
+    tensors (no host copy of the whole bank)."""
+    import torch
+
+    E = len(experts)
+    pw13 = torch.empty((E, 2 * inter, hidden // 8), dtype=torch.int32, device=device)
+    s13 = torch.empty((E, 2 * inter, hidden // GROUP), dtype=torch.bfloat16, device=device)
+    pw2 = torch.empty((E, hidden, inter // 8), dtype=torch.int32, device=device)
+    s2 = torch.empty((E, hidden, inter // GROUP), dtype=torch.bfloat16, device=device)
+    for i, e in enumerate(experts):
+        a, b, c, d = expert_weights(seed, e, hidden, inter)
+        pw13[i].copy_(to_device(a, device))
+        s13[i].copy_(to_device(b, device))
+        pw2[i].copy_(to_device(c, device))
+        s2[i].copy_(to_device(d, device))
+    return dict(packed_w13=pw13, scales_w13=s13, packed_w2=pw2, scales_w2=s2)
+
+
+def compact_routing(topk_ids: np.ndarray, rows, expert_base: int, n_local: int):
+    """For the tokens `rows`: the sorted global ids of the local experts they
+    use, and their ids renumbered into that list (non-local ids -> -1)."""
+    ids = np.asarray(topk_ids)[np.asarray(rows)]
+    local = (ids >= expert_base) & (ids < expert_base + n_local)
+    used = np.unique(ids[local])
+    remap = np.full(ids.shape, -1, np.int32)
+    remap[local] = np.searchsorted(used, ids[local]).astype(np.int32)
+    return [int(u) for u in used], remap

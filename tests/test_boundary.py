@@ -1,0 +1,159 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+symbol the header declares, and rejects every invalid argument before any
+launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a16_int4_grouped_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from w4a16_int4_grouped_moe_amd import build
+
+        build.build()
+    return moe.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_w4a16_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted([
+        "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_forward",
+        "moe_w4a16_forward_block_m", "moe_w4a16_forward_timed", "moe_w4a16_status_string",
+        "moe_w4a16_workspace_size"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_codes_match_header(lib):
+    text = open(HEADER).read()
+    for name in ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGNMENT",
+                 "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP"]:
+        m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
+        assert m and int(m.group(1)) == getattr(moe, name), name
+        assert moe.status_string(getattr(moe, name)).startswith(name)
+
+
+def P(**kw):
+    base = dict(num_tokens=64, hidden=7168, inter=2048, num_experts=384, top_k=8,
+                expert_base=0, group_size=32)
+    base.update(kw)
+    return moe.problem(**base)
+
+
+def test_workspace_size_and_block_m(lib):
+    p = P()
+    assert moe.forward_block_m(p) == 16
+    assert moe.forward_block_m(P(num_tokens=4096)) == 64
+    n = moe.workspace_size(p)
+    T, H, I, k = 64, 7168, 2048, 8
+    cap = T * k + min(384, T * k) * 15
+    # at least: bucket arrays, h rows, per-pair y, shared h and s
+    assert n >= 4 * cap + 2 * cap * I + 4 * T * k * H + 2 * T * I + 4 * T * H
+    assert n < 1.2 * (4 * cap + 2 * cap * I + 4 * T * k * H + 2 * T * I + 4 * T * H) + 4096
+    assert moe.workspace_size(P(num_tokens=0)) == 0
+    assert moe.align_capacity(p, 16) == (cap, cap // 16)
+    assert moe.align_capacity(P(num_tokens=1), 16) == (8 + 8 * 15, (8 + 8 * 15) // 16)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=7100), moe.MOE_ERR_SHAPE),
+    (dict(hidden=96), moe.MOE_ERR_SHAPE),
+    (dict(inter=2000), moe.MOE_ERR_SHAPE),
+    (dict(top_k=0), moe.MOE_ERR_SHAPE),
+    (dict(top_k=17), moe.MOE_ERR_SHAPE),
+    (dict(num_experts=0), moe.MOE_ERR_SHAPE),
+    (dict(num_experts=513), moe.MOE_ERR_UNSUPPORTED),
+    (dict(group_size=64), moe.MOE_ERR_UNSUPPORTED),
+    (dict(group_size=128), moe.MOE_ERR_UNSUPPORTED),
+    (dict(num_tokens=-1), moe.MOE_ERR_SHAPE),
+    (dict(expert_base=-1), moe.MOE_ERR_SHAPE),
+    (dict(num_tokens=1 << 28), moe.MOE_ERR_SHAPE),
+])
+def test_invalid_problem_rejected(lib, kw, status):
+    p = P(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_w4a16_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 9
+    assert lib.moe_w4a16_forward(*args, ctypes.byref(p), fake, 1 << 40, None) == status
+
+
+def _fwd(lib, p, ptrs, ws_bytes=1 << 40):
+    return lib.moe_w4a16_forward(*ptrs, ctypes.byref(p), ctypes.c_void_p(0x20000), ws_bytes,
+                                 None)
+
+
+def test_forward_argument_errors_before_launch(lib):
+    p = P()
+    good = [ctypes.c_void_p(0x10000 + 0x100 * i) for i in range(9)]
+    assert lib.moe_w4a16_forward(*good, None, ctypes.c_void_p(0x20000), 1 << 40, None) == \
+        moe.MOE_ERR_NULL
+    for i in range(9):
+        ptrs = list(good)
+        ptrs[i] = None
+        want = moe.MOE_OK if i == 7 else moe.MOE_ERR_NULL  # shared_w is optional
+        if want == moe.MOE_OK:
+            continue  # a valid call would launch; not on the CPU
+        assert _fwd(lib, p, ptrs) == want, i
+        ptrs[i] = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+        assert _fwd(lib, p, ptrs) == moe.MOE_ERR_ALIGNMENT, i
+    assert lib.moe_w4a16_forward(*good, ctypes.byref(p), None, 1 << 40, None) == moe.MOE_ERR_NULL
+    need = moe.workspace_size(p)
+    assert _fwd(lib, p, good, need - 1) == moe.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    assert lib.moe_w4a16_forward(*good, ctypes.byref(p), ctypes.c_void_p(0x20004), 1 << 40,
+                                 None) == moe.MOE_ERR_ALIGNMENT
+
+
+def test_zero_tokens_is_a_noop(lib):
+    p = P(num_tokens=0)
+    # no pointer is touched and nothing is launched
+    assert lib.moe_w4a16_forward(*([None] * 9), ctypes.byref(p), None, 0, None) == moe.MOE_OK
+
+
+def test_align_argument_errors(lib):
+    p = P()
+    cap_s, cap_b = moe.align_capacity(p, 16)
+    f = ctypes.c_void_p
+    ok = dict(ids=f(0x10000), sorted=f(0x20000), blocks=f(0x30000), npad=f(0x40000))
+
+    def call(bm=16, cs=cap_s, cb=cap_b, **over):
+        a = dict(ok, **over)
+        return lib.moe_w4a16_align(a["ids"], ctypes.byref(p), bm, a["sorted"], cs, a["blocks"],
+                                   cb, a["npad"], None)
+
+    assert call(bm=0) == moe.MOE_ERR_SHAPE
+    assert call(bm=2048) == moe.MOE_ERR_SHAPE
+    assert call(cs=cap_s - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(cb=cap_b - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(ids=None) == moe.MOE_ERR_NULL
+    assert call(npad=None) == moe.MOE_ERR_NULL
+    assert call(sorted=f(0x20004)) == moe.MOE_ERR_ALIGNMENT
+    with pytest.raises(ValueError):
+        moe.align_capacity(p, 0)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from w4a16_int4_grouped_moe_amd import _binding
+
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.library()

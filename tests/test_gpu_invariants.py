@@ -1,0 +1,118 @@
+"""Properties of the HIP path that hold at any size: determinism, zero and
+invalid routing, exact power-of-two scaling, token permutation, empty input,
+and replay of a captured HIP graph."""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from tests.helpers import run_layer
+
+pytestmark = pytest.mark.gpu
+
+H, I, E, K, T = 512, 256, 16, 4, 96
+
+
+@pytest.fixture(scope="module")
+def setup():
+    import torch
+
+    dev = torch.device("cuda:0")
+    bank = mi.weight_bank(3, H, I, list(range(E)))
+    bank_dev = {k: mi.to_device(v, dev) for k, v in bank.__dict__.items()}
+    x = mi.activations(4, T, H)
+    ids, w = mi.routing_uniform(5, T, E, K)
+    sw = mi.shared_weights(3, H, I)
+    return dev, bank, bank_dev, x, ids, w, sw
+
+
+def bits(t):
+    import torch
+
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().copy()
+
+
+def test_deterministic(setup):
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    a = bits(run_layer(dev, x, ids, w, bank_dev, sw))
+    for _ in range(10):
+        assert np.array_equal(bits(run_layer(dev, x, ids, w, bank_dev, sw)), a)
+
+
+def test_zero_weights_and_invalid_ids_give_shared_only(setup):
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    a = bits(run_layer(dev, x, ids, np.zeros_like(w), bank_dev, sw))
+    b = bits(run_layer(dev, x, np.full_like(ids, -1), w, bank_dev, sw))
+    c = bits(run_layer(dev, x, ids + E, w, bank_dev, sw))  # all ids beyond the local range
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    # and without a shared expert the output is exactly zero
+    z = bits(run_layer(dev, x, np.full_like(ids, -1), w, bank_dev, None))
+    assert not z.any()
+
+
+def test_doubling_down_scales_doubles_output_exactly(setup):
+    import torch
+
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    base = run_layer(dev, x, ids, w, bank_dev, None)
+    doubled_dev = dict(bank_dev)
+    doubled_dev["scales_w2"] = bank_dev["scales_w2"] * 2
+    dbl = run_layer(dev, x, ids, w, doubled_dev, None)
+    torch.cuda.synchronize()
+    assert torch.equal(dbl.float(), 2 * base.float())
+
+
+def test_token_permutation(setup):
+    import torch
+
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    perm = np.random.default_rng(1).permutation(T)
+    a = run_layer(dev, x, ids, w, bank_dev, sw).float()
+    b = run_layer(dev, x[perm], ids[perm], w[perm], bank_dev, sw).float()
+    torch.cuda.synchronize()
+    assert torch.equal(a[torch.from_numpy(perm).to(dev)], b)
+
+
+def test_empty_batch(setup):
+    import torch
+
+    import w4a16_int4_grouped_moe_amd as moe
+
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    out = run_layer(dev, x[:0], ids[:0], w[:0], bank_dev, sw)
+    assert out.shape == (0, H)
+    p = moe.problem(0, H, I, E, K)
+    assert moe.workspace_size(p) == 0
+
+
+def test_graph_capture_replay(setup):
+    import torch
+
+    import w4a16_int4_grouped_moe_amd as moe
+
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    d = lambda a: mi.to_device(a, dev)
+    xs, ids_d, w_d, sw_d = d(x), d(ids), d(w), d(sw)
+    p = moe.problem(T, H, I, E, K)
+    ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    args = (xs, ids_d, w_d, bank_dev["packed_w13"], bank_dev["scales_w13"],
+            bank_dev["packed_w2"], bank_dev["scales_w2"], sw_d)
+    eager = moe.forward(*args, workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(*args, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(*args, out=out, workspace=ws)
+    for i in range(4):
+        out.zero_()
+        ws.fill_(0xFF)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        # unrelated eager work between replays
+        moe.forward(xs[:7], ids_d[:7], w_d[:7], *args[3:])
+        torch.cuda.synchronize()

@@ -1,0 +1,116 @@
+"""Layer parity: the HIP path against the fp64 oracle, elementwise, on the
+seeded synthetic workloads (full rows where the oracle is quick, sampled
+tokens at full size -- tokens are independent, so a sampled row is checked
+exactly as in a full run)."""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from tests.helpers import check, oracle_rows, run_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------- tiny shapes
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("T", [1, 5, 16, 100])
+def test_tiny(dev, shared, T):
+    import torch
+
+    g = mi.TINY
+    bank = mi.weight_bank(5, g.hidden, g.inter, list(range(g.n_experts)))
+    bank_dev = {k: mi.to_device(v, dev) for k, v in bank.__dict__.items()}
+    x = mi.activations(6 + T, T, g.hidden)
+    ids, w = mi.routing_uniform(7 + T, T, g.n_experts, g.top_k)
+    sw = mi.shared_weights(5, g.hidden, g.inter) if shared else None
+    print(f"[case] tiny T={T} shared={shared}", flush=True)
+    out = run_layer(dev, x, ids, w, bank_dev, sw)
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw)
+    check(mi.bf16_tensor_to_f64(out), ref, f"tiny T={T} shared={shared}")
+
+
+@pytest.mark.parametrize("T,E,k,base,bm_rows", [
+    (300, 12, 4, 0, "many rows per expert"),
+    (40, 20, 6, 5, "expert base with invalid ids"),
+])
+def test_mid_shapes(dev, T, E, k, base, bm_rows):
+    import torch
+
+    H, I = 512, 384
+    n_global = base + E + 4
+    bank = mi.weight_bank(9, H, I, list(range(base, base + E)))
+    bank_dev = {kk: mi.to_device(v, dev) for kk, v in bank.__dict__.items()}
+    x = mi.activations(10, T, H)
+    ids, w = mi.routing_uniform(11, T, n_global, k)
+    ids[::7, 0] = -1
+    sw = mi.shared_weights(9, H, I)
+    print(f"[case] mid T={T} E={E} k={k} base={base}", flush=True)
+    out = run_layer(dev, x, ids, w, bank_dev, sw, expert_base=base)
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw, base)
+    check(mi.bf16_tensor_to_f64(out), ref, f"mid T={T} ({bm_rows})")
+
+
+# ------------------------------------------------------- Kimi-K2.6 layer shape
+@pytest.fixture(scope="module")
+def kimi(dev):
+    g = mi.KIMI
+    print("[fixture] generating the 384-expert Kimi-shape bank on the device", flush=True)
+    bank = mi.device_bank(1, g.hidden, g.inter, list(range(g.n_experts)), dev)
+    shared = mi.shared_weights(1, g.hidden, g.inter)
+    return bank, shared
+
+
+def _kimi_case(dev, kimi, name, T, rows=None, n_sample=None):
+    import torch
+
+    bank, shared = kimi
+    w = mi.workload(name, T)
+    g = w.geo
+    x = mi.activations(w.seed_x + w.T, w.T, g.hidden)
+    ids, wts = mi.make_routing(w)
+    if rows is None:
+        rows = np.arange(T) if n_sample is None else np.sort(
+            np.random.default_rng(T).choice(T, n_sample, replace=False))
+    print(f"[case] {name} T={T} rows={len(rows)}", flush=True)
+    sub = {k: v[w.expert_base:w.expert_base + w.n_local] for k, v in bank.items()}
+    out = run_layer(dev, x, ids, wts, sub, shared, expert_base=w.expert_base)
+    torch.cuda.synchronize()
+    got = mi.bf16_tensor_to_f64(out)
+    assert np.isfinite(got).all()
+    ref = oracle_rows(w.seed_bank, g, x, ids, wts, shared, w.expert_base, w.n_local, rows)
+    return check(got[rows], ref, f"{name} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_kimi_decode(dev, kimi, T):
+    _kimi_case(dev, kimi, "decode", T)
+
+
+def test_kimi_prefill_sampled(dev, kimi):
+    _kimi_case(dev, kimi, "prefill", 4096, n_sample=10)
+
+
+def test_kimi_skew_sampled(dev, kimi):
+    w = mi.workload("skew", 512)
+    ids, _ = mi.make_routing(w)
+    hot = np.bincount(ids.ravel(), minlength=384).argmax()
+    hot_rows = np.nonzero((ids == hot).any(1))[0]
+    rows = np.unique(np.concatenate([hot_rows[:4], hot_rows[-2:], [0, 255, 511]]))
+    _kimi_case(dev, kimi, "skew", 512, rows=rows)
+
+
+def test_kimi_expert_parallel_share_sampled(dev, kimi):
+    _kimi_case(dev, kimi, "ep", 2048, n_sample=12)

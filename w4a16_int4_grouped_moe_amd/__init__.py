@@ -1,0 +1,29 @@
+"""MI355X (gfx950) W4A16 INT4 grouped MoE layer.
+
+A thin binding over the C ABI declared in include/moe_w4a16.h: argument
+marshalling only, every step of the layer runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.
+
+    out = forward(x, topk_ids, topk_weights, packed_w13, scales_w13,
+                  packed_w2, scales_w2, shared_w=None, out=None, expert_base=0)
+"""
+from ._binding import (  # noqa: F401
+    MOE_ERR_ALIGNMENT,
+    MOE_ERR_HIP,
+    MOE_ERR_NULL,
+    MOE_ERR_SHAPE,
+    MOE_ERR_UNSUPPORTED,
+    MOE_ERR_WORKSPACE,
+    MOE_OK,
+    LIB_PATH,
+    MoeError,
+    Problem,
+    align,
+    align_capacity,
+    forward,
+    forward_block_m,
+    library,
+    problem,
+    status_string,
+    workspace_size,
+)

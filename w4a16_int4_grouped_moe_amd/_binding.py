@@ -1,0 +1,219 @@
+"""ctypes binding of libmoe_w4a16.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_w4a16.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = -1
+MOE_ERR_SHAPE = -2
+MOE_ERR_ALIGNMENT = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_UNSUPPORTED = -5
+MOE_ERR_HIP = -6
+
+GROUP = 32
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("expert_base", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+    ]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def library():
+    """Load the built library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m w4a16_int4_grouped_moe_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(Problem)
+        lib.moe_w4a16_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+        lib.moe_w4a16_forward_block_m.argtypes = [PP, ctypes.POINTER(ctypes.c_int32)]
+        lib.moe_w4a16_align_capacity.argtypes = [PP, ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_int64),
+                                                 ctypes.POINTER(ctypes.c_int64)]
+        lib.moe_w4a16_align.argtypes = [P, PP, ctypes.c_int32, P, ctypes.c_int64, P,
+                                        ctypes.c_int64, P, P]
+        lib.moe_w4a16_forward.argtypes = [P] * 9 + [PP, P, ctypes.c_size_t, P]
+        lib.moe_w4a16_forward_timed.argtypes = [P] * 9 + [PP, P, ctypes.c_size_t, P, P]
+        lib.moe_w4a16_status_string.argtypes = [ctypes.c_int]
+        lib.moe_w4a16_status_string.restype = ctypes.c_char_p
+        for f in ("workspace_size", "forward_block_m", "align_capacity", "align", "forward",
+                  "forward_timed"):
+            getattr(lib, "moe_w4a16_" + f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().moe_w4a16_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        msg = status_string(status)
+        if status == MOE_ERR_HIP:
+            raise MoeError(status, msg)
+        raise ValueError(f"{msg} (status {status})")
+
+
+def problem(num_tokens: int, hidden: int, inter: int, num_experts: int, top_k: int,
+            expert_base: int = 0, group_size: int = GROUP) -> Problem:
+    return Problem(num_tokens, hidden, inter, num_experts, expert_base, top_k, group_size)
+
+
+def workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().moe_w4a16_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def forward_block_m(p: Problem) -> int:
+    v = ctypes.c_int32(0)
+    _check(library().moe_w4a16_forward_block_m(ctypes.byref(p), ctypes.byref(v)))
+    return v.value
+
+
+def align_capacity(p: Problem, block_m: int):
+    s, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(library().moe_w4a16_align_capacity(ctypes.byref(p), block_m, ctypes.byref(s),
+                                              ctypes.byref(b)))
+    return s.value, b.value
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_handle(device) -> Optional[int]:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, ndim, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+            shared_w=None, out=None, expert_base: int = 0, workspace=None,
+            stage_events=None):
+    """The W4A16 MoE layer (see include/moe_w4a16.h for the definition).
+
+    x bf16 [T, H]; topk_ids int32 [T, k]; topk_weights fp32 [T, k];
+    packed_w13 int32 [E, 2I, H/8]; scales_w13 bf16 [E, 2I, H/32];
+    packed_w2 int32 [E, H, I/8]; scales_w2 bf16 [E, H, I/32];
+    shared_w bf16 [2I*H + H*I] or None. Returns out bf16 [T, H].
+    stage_events: optional sequence of 5 raw hipEvent_t handles (int or None)
+    recorded between the stages (see moe_w4a16_forward_timed).
+    """
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    _need(x, "x", torch.bfloat16, 2, dev)
+    T, H = x.shape
+    _need(topk_ids, "topk_ids", torch.int32, 2, dev)
+    k = topk_ids.shape[1]
+    _need(topk_weights, "topk_weights", torch.float32, 2, dev)
+    _need(packed_w13, "packed_w13", torch.int32, 3, dev)
+    E, I2, _ = packed_w13.shape
+    I = I2 // 2
+    _need(scales_w13, "scales_w13", torch.bfloat16, 3, dev)
+    _need(packed_w2, "packed_w2", torch.int32, 3, dev)
+    _need(scales_w2, "scales_w2", torch.bfloat16, 3, dev)
+    shapes = {
+        "topk_ids": (tuple(topk_ids.shape), (T, k)),
+        "topk_weights": (tuple(topk_weights.shape), (T, k)),
+        "packed_w13": (tuple(packed_w13.shape), (E, 2 * I, H // 8)),
+        "scales_w13": (tuple(scales_w13.shape), (E, 2 * I, H // GROUP)),
+        "packed_w2": (tuple(packed_w2.shape), (E, H, I // 8)),
+        "scales_w2": (tuple(scales_w2.shape), (E, H, I // GROUP)),
+    }
+    for name, (got, want) in shapes.items():
+        if got != want:
+            raise ValueError(f"{name} has shape {got}, expected {want}")
+    if shared_w is not None:
+        _need(shared_w, "shared_w", torch.bfloat16, 1, dev)
+        if shared_w.numel() != 3 * I * H:
+            raise ValueError(f"shared_w must hold {3 * I * H} values")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 2, dev)
+        if tuple(out.shape) != (T, H):
+            raise ValueError("out must be [T, H]")
+    p = problem(T, H, I, E, k, expert_base)
+    need = workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    args = (x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), packed_w13.data_ptr(),
+            scales_w13.data_ptr(), packed_w2.data_ptr(), scales_w2.data_ptr(),
+            None if shared_w is None else shared_w.data_ptr(), out.data_ptr(), ctypes.byref(p),
+            workspace.data_ptr(), workspace.numel(), _stream_handle(dev))
+    if stage_events is None:
+        st = library().moe_w4a16_forward(*args)
+    else:
+        if len(stage_events) != 5:
+            raise ValueError("stage_events needs 5 entries")
+        ev = (ctypes.c_void_p * 5)(*[e or None for e in stage_events])
+        st = library().moe_w4a16_forward_timed(*args, ev)
+    _check(st)
+    return out
+
+
+def align(topk_ids, num_experts: int, block_m: int, expert_base: int = 0):
+    """Token/expert bucketing: returns (sorted_ids, block_expert, n_padded)
+    int32 device tensors sized to the capacities; only the first n_padded
+    sorted_ids and n_padded/block_m block_expert entries are meaningful."""
+    torch = _torch()
+    dev = topk_ids.device
+    _need(topk_ids, "topk_ids", torch.int32, 2, dev)
+    T, k = topk_ids.shape
+    p = problem(T, 128, 128, num_experts, k, expert_base)
+    cap_s, cap_b = align_capacity(p, block_m)
+    sorted_ids = torch.empty(max(cap_s, 4), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap_b, 4), dtype=torch.int32, device=dev)
+    n_padded = torch.empty(4, dtype=torch.int32, device=dev)
+    st = library().moe_w4a16_align(
+        topk_ids.data_ptr(), ctypes.byref(p), block_m, sorted_ids.data_ptr(), cap_s,
+        block_expert.data_ptr(), cap_b, n_padded.data_ptr(), _stream_handle(dev))
+    _check(st)
+    return sorted_ids, block_expert, n_padded[:1]

@@ -1,0 +1,248 @@
+// api.cpp -- host side of the W4A16 MoE C ABI: argument validation, workspace
+// layout and the launch sequence align -> gate_up(+SwiGLU) -> down -> combine.
+// Every check runs before the first launch; nothing is allocated and the host
+// never waits on the device.
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe_w4a16.h"
+#include "internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxPairs = 0x7ffffffe;  // T*k and the sentinel T*k fit in int32
+
+thread_local char g_status_msg[256];
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_problem(const moe_w4a16_problem* p) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->group_size != 32) return MOE_ERR_UNSUPPORTED;
+  if (p->num_tokens < 0 || p->hidden <= 0 || p->inter <= 0 || p->num_experts <= 0 ||
+      p->top_k <= 0 || p->top_k > MOE_MAX_TOP_K || p->expert_base < 0)
+    return MOE_ERR_SHAPE;
+  if (p->hidden % 128 != 0 || p->inter % 128 != 0) return MOE_ERR_SHAPE;
+  if (p->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)p->expert_base + p->num_experts > 0x7fffffff) return MOE_ERR_SHAPE;
+  if (p->num_tokens > kMaxPairs / p->top_k) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int64_t sorted_capacity(const moe_w4a16_problem* p, int32_t bm) {
+  const int64_t P = p->num_tokens * p->top_k;
+  const int64_t emin = P < p->num_experts ? P : p->num_experts;
+  return P + emin * (bm - 1);
+}
+
+int32_t choose_block_m(const moe_w4a16_problem* p) {
+  // many rows per expert -> 64-row blocks (dequantisation amortised over more
+  // rows); otherwise 16-row blocks (less padding)
+  const int64_t P = p->num_tokens * p->top_k;
+  return P >= 32 * (int64_t)p->num_experts ? 64 : 16;
+}
+
+struct Layout {
+  size_t sorted_ids, block_expert, meta, h, y, hs, s, total;
+  int64_t cap_rows;
+  int32_t max_blocks, bm;
+};
+
+Layout layout(const moe_w4a16_problem* p) {
+  Layout L{};
+  L.bm = choose_block_m(p);
+  L.cap_rows = sorted_capacity(p, L.bm);
+  L.max_blocks = (int32_t)(L.cap_rows / L.bm);
+  const size_t T = (size_t)p->num_tokens, H = (size_t)p->hidden, I = (size_t)p->inter;
+  const size_t P = T * (size_t)p->top_k;
+  size_t o = 0;
+  L.sorted_ids = o; o = round_up(o + 4 * (size_t)L.cap_rows);
+  L.block_expert = o; o = round_up(o + 4 * (size_t)L.max_blocks);
+  L.meta = o; o = round_up(o + 64);
+  L.h = o; o = round_up(o + 2 * (size_t)L.max_blocks * L.bm * I);
+  L.y = o; o = round_up(o + 4 * P * H);
+  L.hs = o; o = round_up(o + 2 * T * I);
+  L.s = o; o = round_up(o + 4 * T * H);
+  L.total = o;
+  return L;
+}
+
+int hip_status(hipError_t err) {
+  if (err == hipSuccess) return MOE_OK;
+  snprintf(g_status_msg, sizeof g_status_msg, "HIP error %d (%s): %s", (int)err,
+           hipGetErrorName(err), hipGetErrorString(err));
+  return MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_w4a16_workspace_size(const moe_w4a16_problem* p, size_t* bytes) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = p->num_tokens == 0 ? 0 : layout(p).total;
+  return MOE_OK;
+}
+
+int moe_w4a16_forward_block_m(const moe_w4a16_problem* p, int32_t* block_m) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!block_m) return MOE_ERR_NULL;
+  *block_m = choose_block_m(p);
+  return MOE_OK;
+}
+
+int moe_w4a16_align_capacity(const moe_w4a16_problem* p, int32_t block_m,
+                             int64_t* sorted_cap, int64_t* block_cap) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!sorted_cap || !block_cap) return MOE_ERR_NULL;
+  if (block_m < 1 || block_m > 1024) return MOE_ERR_SHAPE;
+  *sorted_cap = sorted_capacity(p, block_m);
+  *block_cap = *sorted_cap / block_m;
+  return MOE_OK;
+}
+
+int moe_w4a16_align(const int32_t* topk_ids, const moe_w4a16_problem* p, int32_t block_m,
+                    int32_t* sorted_ids, int64_t sorted_cap, int32_t* block_expert,
+                    int64_t block_cap, int32_t* n_padded, void* stream) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (block_m < 1 || block_m > 1024) return MOE_ERR_SHAPE;
+  if (!n_padded) return MOE_ERR_NULL;
+  const int64_t need = sorted_capacity(p, block_m);
+  if (p->num_tokens > 0 && (!topk_ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
+  if (!aligned16(topk_ids) || !aligned16(sorted_ids) || !aligned16(block_expert) ||
+      !aligned16(n_padded))
+    return MOE_ERR_ALIGNMENT;
+  if (sorted_cap < need || block_cap < need / block_m) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_align(topk_ids, p->num_tokens * p->top_k, p->num_experts,
+                                      p->expert_base, block_m, sorted_ids, block_expert,
+                                      n_padded, (hipStream_t)stream));
+}
+
+static int forward_impl(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                        const int32_t* packed_w13, const void* scales_w13,
+                        const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
+                        void* out, const moe_w4a16_problem* p, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* events) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->num_tokens == 0) return MOE_OK;
+  if (!x || !topk_ids || !topk_weights || !packed_w13 || !scales_w13 || !packed_w2 ||
+      !scales_w2 || !out || !workspace)
+    return MOE_ERR_NULL;
+  const void* ptrs[] = {x, topk_ids, topk_weights, packed_w13, scales_w13,
+                        packed_w2, scales_w2, shared_w, out, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return MOE_ERR_ALIGNMENT;
+  const Layout L = layout(p);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted_ids);
+  int32_t* blk = reinterpret_cast<int32_t*>(ws + L.block_expert);
+  int32_t* n_padded = reinterpret_cast<int32_t*>(ws + L.meta);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  uint16_t* hs = reinterpret_cast<uint16_t*>(ws + L.hs);
+  float* s = reinterpret_cast<float*>(ws + L.s);
+  hipStream_t strm = (hipStream_t)stream;
+
+  const int64_t T = p->num_tokens;
+  const int32_t H = p->hidden, I = p->inter, E = p->num_experts, k = p->top_k;
+  const uint16_t* sw = static_cast<const uint16_t*>(shared_w);
+
+  auto mark = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord((hipEvent_t)events[i], strm);
+    return hipSuccess;
+  };
+  hipError_t err = mark(0);
+  if (err != hipSuccess) return hip_status(err);
+  err = moe::launch_align(topk_ids, T * k, E, p->expert_base, L.bm, sorted, blk,
+                                     n_padded, strm);
+  if (err != hipSuccess) return hip_status(err);
+
+  moe::GemmParams g{};
+  g.sorted_ids = sorted;
+  g.block_expert = blk;
+  g.n_padded = n_padded;
+  g.max_blocks = L.max_blocks;
+  g.T = T;
+  g.P = T * k;
+  g.k = k;
+  g.I = I;
+
+  // gate_up + SwiGLU
+  g.a_routed = static_cast<const uint16_t*>(x);
+  g.packed = packed_w13;
+  g.scales = static_cast<const uint16_t*>(scales_w13);
+  g.a_shared = static_cast<const uint16_t*>(x);
+  g.wshared = sw;
+  g.h_routed = h;
+  g.h_shared = hs;
+  g.K = H;
+  g.N = I;
+  if ((err = mark(1)) != hipSuccess) return hip_status(err);
+  err = moe::launch_gate_up(g, L.bm, strm);
+  if (err != hipSuccess) return hip_status(err);
+
+  // down
+  g.a_routed = h;
+  g.packed = packed_w2;
+  g.scales = static_cast<const uint16_t*>(scales_w2);
+  g.a_shared = hs;
+  g.wshared = sw ? sw + (size_t)2 * I * H : nullptr;
+  g.y_routed = y;
+  g.y_shared = s;
+  g.K = I;
+  g.N = H;
+  if ((err = mark(2)) != hipSuccess) return hip_status(err);
+  err = moe::launch_down(g, L.bm, strm);
+  if (err != hipSuccess) return hip_status(err);
+
+  if ((err = mark(3)) != hipSuccess) return hip_status(err);
+  err = moe::launch_combine(y, sw ? s : nullptr, topk_ids, topk_weights,
+                            static_cast<uint16_t*>(out), T, H, k, E, p->expert_base, strm);
+  if (err != hipSuccess) return hip_status(err);
+  return hip_status(mark(4));
+}
+
+int moe_w4a16_forward(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                      const int32_t* packed_w13, const void* scales_w13,
+                      const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
+                      void* out, const moe_w4a16_problem* p, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+                      shared_w, out, p, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_w4a16_forward_timed(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                            const int32_t* packed_w13, const void* scales_w13,
+                            const int32_t* packed_w2, const void* scales_w2,
+                            const void* shared_w, void* out, const moe_w4a16_problem* p,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* stage_events) {
+  return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+                      shared_w, out, p, workspace, workspace_bytes, stream, stage_events);
+}
+
+const char* moe_w4a16_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range";
+    case MOE_ERR_ALIGNMENT: return "MOE_ERR_ALIGNMENT: a device pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace or buffer too small";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported configuration";
+    case MOE_ERR_HIP: return g_status_msg[0] ? g_status_msg : "MOE_ERR_HIP: a HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// internal.h -- launch interfaces shared by the host library and the kernels
+// of the W4A16 MoE layer. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Bucketing: stable counting sort of valid (token, slot) pairs by local expert.
+// One work-group; E <= 1024.
+hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
+                        int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                        int32_t* n_padded, hipStream_t stream);
+
+// Operands of one grouped-GEMM launch (routed blocks followed by shared-expert
+// row tiles). Widths are in elements.
+struct GemmParams {
+  // routed part
+  const uint16_t* a_routed;     // gate_up: x [T, H]; down: h [rows, I] (sorted order)
+  const int32_t* sorted_ids;    // [max_blocks * bm]
+  const int32_t* block_expert;  // [max_blocks]
+  const int32_t* n_padded;      // [1]
+  const int32_t* packed;        // int4 codes [E, Nw, K/8]
+  const uint16_t* scales;       // bf16 [E, Nw, K/32]
+  int32_t max_blocks;
+  // shared part (absent when wshared == nullptr)
+  const uint16_t* a_shared;     // gate_up: x [T, H]; down: hs [T, I]
+  const uint16_t* wshared;      // bf16 [Nw, K]
+  // outputs
+  uint16_t* h_routed;           // gate_up: h [max_blocks * bm, I]
+  uint16_t* h_shared;           // gate_up: hs [T, I]
+  float* y_routed;              // down: y [T*k, H], row = pair id
+  float* y_shared;              // down: s [T, H]
+  // sizes
+  int64_t T;
+  int64_t P;                    // T * k (sentinel value)
+  int32_t k;
+  int32_t K;                    // reduction width (H for gate_up, I for down)
+  int32_t I;                    // intermediate width
+  int32_t N;                    // output width (I for gate_up, H for down)
+};
+
+hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stream);
+hipError_t launch_down(const GemmParams& p, int32_t block_m, hipStream_t stream);
+
+// out[t] = bf16(s[t] + sum_j valid * w[t,j] * y[t*k+j]), fp32 sum in slot order.
+hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
+                          const float* topk_weights, uint16_t* out, int64_t T, int32_t H,
+                          int32_t k, int32_t E, int32_t base, hipStream_t stream);
+
+}  // namespace moe
