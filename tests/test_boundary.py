@@ -59,16 +59,17 @@ def P(**kw):
 
 def test_workspace_size_and_block_m(lib):
     p = P()
-    assert moe.forward_block_m(p) == 16
+    assert moe.forward_block_m(p) == 4
+    assert moe.forward_block_m(P(num_tokens=512)) == 16
     assert moe.forward_block_m(P(num_tokens=4096)) == 64
     n = moe.workspace_size(p)
     T, H, I, k = 64, 7168, 2048, 8
-    cap = T * k + min(384, T * k) * 15
+    cap = T * k + min(384, T * k) * 3
     # at least: bucket arrays, h rows, per-pair y, shared h and s
     assert n >= 4 * cap + 2 * cap * I + 4 * T * k * H + 2 * T * I + 4 * T * H
     assert n < 1.2 * (4 * cap + 2 * cap * I + 4 * T * k * H + 2 * T * I + 4 * T * H) + 4096
     assert moe.workspace_size(P(num_tokens=0)) == 0
-    assert moe.align_capacity(p, 16) == (cap, cap // 16)
+    assert moe.align_capacity(p, 4) == (cap, cap // 4)
     assert moe.align_capacity(P(num_tokens=1), 16) == (8 + 8 * 15, (8 + 8 * 15) // 16)
 
 

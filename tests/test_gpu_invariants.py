@@ -9,13 +9,14 @@ from tests.helpers import run_layer
 
 pytestmark = pytest.mark.gpu
 
-H, I, E, K, T = 512, 256, 16, 4, 96
+H, I, E, K = 512, 256, 16, 4
 
 
-@pytest.fixture(scope="module")
-def setup():
+@pytest.fixture(scope="module", params=[96, 8], ids=["tiled", "small-batch"])
+def setup(request):
     import torch
 
+    T = request.param
     dev = torch.device("cuda:0")
     bank = mi.weight_bank(3, H, I, list(range(E)))
     bank_dev = {k: mi.to_device(v, dev) for k, v in bank.__dict__.items()}
@@ -66,7 +67,7 @@ def test_token_permutation(setup):
     import torch
 
     dev, bank, bank_dev, x, ids, w, sw = setup
-    perm = np.random.default_rng(1).permutation(T)
+    perm = np.random.default_rng(1).permutation(x.shape[0])
     a = run_layer(dev, x, ids, w, bank_dev, sw).float()
     b = run_layer(dev, x[perm], ids[perm], w[perm], bank_dev, sw).float()
     torch.cuda.synchronize()
@@ -93,6 +94,7 @@ def test_graph_capture_replay(setup):
     dev, bank, bank_dev, x, ids, w, sw = setup
     d = lambda a: mi.to_device(a, dev)
     xs, ids_d, w_d, sw_d = d(x), d(ids), d(w), d(sw)
+    T = x.shape[0]
     p = moe.problem(T, H, I, E, K)
     ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)

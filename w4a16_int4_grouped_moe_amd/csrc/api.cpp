@@ -39,10 +39,13 @@ int64_t sorted_capacity(const moe_w4a16_problem* p, int32_t bm) {
 }
 
 int32_t choose_block_m(const moe_w4a16_problem* p) {
-  // many rows per expert -> 64-row blocks (dequantisation amortised over more
-  // rows); otherwise 16-row blocks (less padding)
+  // About one row per expert (decode): 4-row buckets and the weight-streaming
+  // small-batch kernels. Many rows per expert: 64-row blocks (dequantisation
+  // amortised over more rows). In between: 16-row blocks.
   const int64_t P = p->num_tokens * p->top_k;
-  return P >= 32 * (int64_t)p->num_experts ? 64 : 16;
+  const int64_t E = p->num_experts;
+  if (P <= 4 * E) return 4;
+  return P >= 32 * E ? 64 : 16;
 }
 
 struct Layout {
@@ -189,7 +192,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.K = H;
   g.N = I;
   if ((err = mark(1)) != hipSuccess) return hip_status(err);
-  err = moe::launch_gate_up(g, L.bm, strm);
+  err = L.bm == 4 ? moe::launch_gate_up_small(g, strm) : moe::launch_gate_up(g, L.bm, strm);
   if (err != hipSuccess) return hip_status(err);
 
   // down
@@ -203,7 +206,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.K = I;
   g.N = H;
   if ((err = mark(2)) != hipSuccess) return hip_status(err);
-  err = moe::launch_down(g, L.bm, strm);
+  err = L.bm == 4 ? moe::launch_down_small(g, strm) : moe::launch_down(g, L.bm, strm);
   if (err != hipSuccess) return hip_status(err);
 
   if ((err = mark(3)) != hipSuccess) return hip_status(err);

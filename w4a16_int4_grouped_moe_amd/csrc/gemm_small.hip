@@ -1,0 +1,490 @@
+// gemm_small.hip -- grouped W4A16 GEMMs for small token counts (decode), gfx950.
+//
+// Same two launches as gemm.hip (gate_up with fused SwiGLU, then down), for
+// buckets of at most four rows per expert block. In this regime the layer is
+// bound by the HBM stream of int4 weights, so the kernel is built around that
+// stream and around a cheap, exact dequantisation.
+//
+// Work decomposition. A work-group (4 waves) takes one 4-row block and four
+// consecutive slices of weight rows; each wave owns one slice of NR row-sets of
+// four rows (for gate_up half of them gate rows, half the matching up rows).
+// K advances 16 groups of 32 (512 inputs) per iteration.
+//
+// Data movement per iteration:
+//  * weights: each wave streams its own rows, one 16-byte buffer load per lane
+//    and row-set: lane l = 4*kp + j reads group kp of row j of the row-set, so a
+//    load reads 256 contiguous bytes of each of four rows;
+//  * activations and scales are shared by the four waves: the work-group loads
+//    them once, each thread one coalesced 16-byte piece of each, into LDS
+//    (double buffered, one barrier per iteration). Activations are written in
+//    MFMA fragment order, already permuted for the dequantised weights, so a
+//    wave reads its operands with linear, conflict-free ds_read_b128.
+//
+// Arithmetic: v_mfma_f32_4x4x4_16b_bf16 with its 16 blocks laid along K (block
+// kp = group kp of the iteration): A = the four token rows, B = four weight
+// rows, so activations are not replicated across lanes; the 16 k-parts are
+// summed across lanes once, after the K loop. Dequantisation has no multiply:
+// a 4-bit field u OR-ed into the bf16 pattern 0x4300 is exactly the bf16 value
+// 128 + u (one shift and one v_bitop3 per pair of fields i, i+4), activations
+// are permuted to the same (0,4,1,5 | 2,6,3,7) order, and each group's MFMA
+// chain starts from C0 = -136 * sum(x over the group) -- an MFMA chain of the
+// same activations against the constant bf16 -136 -- so it yields exactly
+// sum x * (u - 8); the group's bf16 scale then multiplies it in fp32 (the
+// weight is never rounded). The bf16 shared expert uses the same structure
+// with its weights taken as they are (natural order, no scales).
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#ifndef MOE_SMALL_NR
+#define MOE_SMALL_NR 4  // int4 row-sets per wave
+#endif
+
+constexpr int kThreads = 256;  // four waves
+constexpr int kWaves = kThreads / 64;
+constexpr int kNR = MOE_SMALL_NR;
+constexpr int kWavesPerSimd = kNR >= 8 ? 2 : 4;  // occupancy target
+constexpr int kNRS = 2;        // bf16 shared-expert row-sets per wave
+constexpr int kTokBlocks = kNR >= 8 ? 4 : 2;  // 4-token blocks per shared-expert work-group
+constexpr int kGroupsPerIt = 16;  // k-parts = MFMA blocks
+constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
+constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
+constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
+constexpr int kXBytes = 4 * 64 * 16;       // activation fragments per iteration
+
+enum { kGateUp = 0, kDown = 1 };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ f32x4 mfma4(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// (a & m) | c in one v_bitop3_b32 (truth table 0xEA over (a, m, c)). The
+// intrinsic keeps the 32-bit form; written as plain and/or, the compiler splits
+// it into 16-bit halves to match the MFMA operand type.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// sum over the 16 k-parts: lanes with equal lane % 4
+__device__ __forceinline__ float kpart_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Output columns per wave slice: gate_up slices cover 2*NR h columns (NR/2
+// gate + NR/2 up row-sets), down slices cover 4*NR output columns.
+template <int PHASE, int NR>
+constexpr int slice_cols() { return PHASE == kGateUp ? 2 * NR : 4 * NR; }
+
+// weight row of row-set rs, row j, of wave slice `slice`
+template <int PHASE, int NR>
+__device__ __forceinline__ int weight_row(const GemmParams& p, int slice, int rs, int j) {
+  if (PHASE == kGateUp) {
+    const int c0 = slice * (2 * NR);
+    return (rs < NR / 2) ? c0 + 4 * rs + j : p.I + c0 + 4 * (rs - NR / 2) + j;
+  }
+  return slice * (4 * NR) + 4 * rs + j;
+}
+
+// LDS of one pipeline stage: activation fragments, then (int4) the scales of
+// the work-group's 4 * 4NR rows for the iteration's 16 groups.
+template <int NR, bool INT4, int NB>
+constexpr int stage_bytes() { return NB * kXBytes + (INT4 ? kWaves * 4 * NR * 32 : 0); }
+
+// NB blocks of four rows starting at row0 (NB > 1 only for the bf16 shared
+// expert: its weights are then read once for 4 NB tokens).
+template <int PHASE, int NR, bool INT4, int NB>
+__device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, int slice0,
+                                           uint8_t* lds) {
+  static_assert(INT4 ? NB == 1 : NB >= 1, "int4 work items hold one block");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kp = lane >> 2;  // k-part: group offset inside an iteration
+  const int j = lane & 3;    // token row (A) and weight row in a row-set (B)
+  const int slice = slice0 + wave;
+  const int K = p.K;
+  const int ngroups = K / 32;
+  const int niters = (ngroups + kGroupsPerIt - 1) / kGroupsPerIt;
+  const int tail = ngroups % kGroupsPerIt;  // groups of the last iteration if partial
+  constexpr int kRowsWG = kWaves * 4 * NR;  // weight rows of the work-group
+
+  // ---- activation staging: thread t -> token row t/64, 16-byte piece t%64 ---
+  // piece c of the row's 1 KB chunk = group c/4, quarter c%4 -> fragment slot
+  // [c%4][lane 4 (c/4) + token]. Rows without data (bucket padding, rows past
+  // the last token of the shared expert) read a real row instead: their
+  // results are never stored and MFMA rows depend only on their own input row.
+  const int xt = tid >> 6;
+  const int xc = tid & 63;
+  const uint16_t* abase;
+  int64_t arows;
+  int xoff[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    int64_t arow;
+    if (INT4) {
+      if (PHASE == kGateUp) {
+        const int32_t pair = p.sorted_ids[row0 + xt];
+        arow = pair < p.P ? pair / p.k : 0;
+        abase = p.a_routed;
+        arows = p.T;
+      } else {
+        arow = row0 + xt;
+        abase = p.a_routed;
+        arows = (int64_t)p.max_blocks * 4;
+      }
+    } else {
+      const int64_t r = row0 + 4 * b + xt;
+      arow = r < p.T ? r : p.T - 1;
+      abase = p.a_shared;
+      arows = p.T;
+    }
+    xoff[b] = (int)(arow * K) * 2 + xc * 16;
+  }
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)abase, 0, (int)(arows * K * 2), kBufferFlags);
+  const int xdst = (xc & 3) * 1024 + ((xc >> 2) * 4 + xt) * 16;
+  const bool xzero_tail = (xc >> 2) >= tail;  // only used in a partial iteration
+
+  // ---- scale staging (int4): thread t < 2*kRowsWG -> row t/2, half t%2 ------
+  const int st_row = tid >> 1;
+  const bool st_active = INT4 && st_row < kRowsWG;
+  __amdgpu_buffer_rsrc_t sres = xres;  // replaced below for int4 weights
+  int soff = 0;
+  const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
+  int e = 0;
+  if (INT4) {
+    e = p.block_expert[row0 / 4];
+    const int64_t r0 = (int64_t)e * Nw;
+    sres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
+                                             Nw * (K / 32) * 2, kBufferFlags);
+    if (st_active) {
+      const int w = st_row / (4 * NR), lr = st_row % (4 * NR);
+      soff = (weight_row<PHASE, NR>(p, slice0 + w, lr / 4, lr % 4) * (K / 32) + 8 * (tid & 1)) * 2;
+    }
+  }
+  const int sdst = NB * kXBytes + tid * 16;  // scale row st_row, half tid & 1
+
+  // ---- weights of this lane ----------------------------------------------
+  __amdgpu_buffer_rsrc_t wres;
+  if (INT4) {
+    const int64_t r0 = (int64_t)e * Nw;
+    wres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.packed + r0 * (K / 8)), 0,
+                                             Nw * (K / 8) * 4, kBufferFlags);
+  } else {
+    wres = __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
+  }
+  int woff[NR];
+#pragma unroll
+  for (int rs = 0; rs < NR; ++rs) {
+    const int row = weight_row<PHASE, NR>(p, slice, rs, j);
+    woff[rs] = INT4 ? (row * (K / 8) + 4 * kp) * 4 : (row * K + 32 * kp) * 2;
+  }
+  // this lane's scales in a stage: row (wave, 4 rs + j), group kp
+  const int sread = NB * kXBytes + (wave * 4 * NR + j) * 32 + kp * 2;
+
+  struct Frag {
+    u32x4 w[NR][INT4 ? 1 : 4];  // int4: 4 words; bf16: 32 weights
+  };
+  auto load_w = [&](Frag& f, int it) {
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) {
+      if (INT4) {
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], it * (kGroupsPerIt * 16), 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          f.w[rs][q] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs] + 16 * q,
+                                                             it * (kGroupsPerIt * 64), 0);
+      }
+    }
+    if (tail && it == niters - 1) {  // groups past the end of K contribute zero
+      if (kp >= tail) {
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs)
+#pragma unroll
+          for (int q = 0; q < (INT4 ? 1 : 4); ++q)
+            f.w[rs][q] = INT4 ? u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u}
+                              : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  // shared stage registers: one activation piece and (int4) one scale piece
+  u32x4 xs_reg[NB], sc_reg = {0, 0, 0, 0};
+  auto load_shared = [&](int it) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      xs_reg[b] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[b], it * (kGroupsPerIt * 64), 0);
+    if (st_active)
+      sc_reg = __builtin_amdgcn_raw_buffer_load_b128(sres, soff, it * (kGroupsPerIt * 2), 0);
+  };
+  auto store_shared = [&](uint8_t* stage, int it) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      u32x4 v = xs_reg[b];
+      if (tail && it == niters - 1 && xzero_tail) v = u32x4{0, 0, 0, 0};
+      if (INT4) {  // (x0..x7) -> (x0,x4,x1,x5 | x2,x6,x3,x7)
+        v = u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
+                  __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                  __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
+                  __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+      }
+      *reinterpret_cast<u32x4*>(stage + b * kXBytes + xdst) = v;
+    }
+    if (st_active) {
+      u32x4 s = sc_reg;
+      if (tail && it == niters - 1) {  // zero scales past the end of K
+        const int g0 = 8 * (tid & 1);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t lo = (g0 + 2 * h) < tail ? (s[h] & 0xFFFFu) : 0u;
+          const uint32_t hi = (g0 + 2 * h + 1) < tail ? (s[h] & 0xFFFF0000u) : 0u;
+          s[h] = lo | hi;
+        }
+      }
+      *reinterpret_cast<u32x4*>(stage + sdst) = s;
+    }
+  };
+
+  f32x4 acc[NB][NR];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) acc[b][rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Frag& f, const uint8_t* stage) {
+    if (INT4) {
+      u32x4 xf[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xf[q] = *reinterpret_cast<const u32x4*>(stage + q * 1024 + lane * 16);
+      // C0 = -136 * (sum of the group's activations), per token row
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+      const u32x2 neg136 = {kNeg136, kNeg136};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c0 = mfma4(u32x2{xf[q][0], xf[q][1]}, neg136, c0);
+        c0 = mfma4(u32x2{xf[q][2], xf[q][3]}, neg136, c0);
+      }
+      // NR independent chains, interleaved so that consecutive MFMAs never
+      // depend on each other
+      f32x4 t[NR];
+#pragma unroll
+      for (int rs = 0; rs < NR; ++rs) t[rs] = c0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x2 b0[NR], b1[NR];
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) {
+          const uint32_t w = f.w[rs][0][q];
+          b0[rs] = u32x2{and_or(w, 0x000F000Fu, kMagic), and_or(w >> 4, 0x000F000Fu, kMagic)};
+          b1[rs] = u32x2{and_or(w >> 8, 0x000F000Fu, kMagic),
+                         and_or(w >> 12, 0x000F000Fu, kMagic)};
+        }
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) t[rs] = mfma4(u32x2{xf[q][0], xf[q][1]}, b0[rs], t[rs]);
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) t[rs] = mfma4(u32x2{xf[q][2], xf[q][3]}, b1[rs], t[rs]);
+      }
+#pragma unroll
+      for (int rs = 0; rs < NR; ++rs) {
+        const uint32_t sb = *reinterpret_cast<const uint16_t*>(stage + sread + rs * 128);
+        acc[0][rs] += bf16_to_f32(sb) * t[rs];
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        u32x4 xf[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xf[q] = *reinterpret_cast<const u32x4*>(stage + b * kXBytes + q * 1024 + lane * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs)
+            acc[b][rs] = mfma4(u32x2{xf[q][0], xf[q][1]}, u32x2{f.w[rs][q][0], f.w[rs][q][1]},
+                               acc[b][rs]);
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs)
+            acc[b][rs] = mfma4(u32x2{xf[q][2], xf[q][3]}, u32x2{f.w[rs][q][2], f.w[rs][q][3]},
+                               acc[b][rs]);
+        }
+      }
+    }
+  };
+
+  // ---- pipeline: stage it+1 loads in flight while stage it is computed ------
+  uint8_t* st0 = lds;
+  uint8_t* st1 = lds + stage_bytes<NR, INT4, NB>();
+  Frag fa, fb;
+  load_shared(0);
+  load_w(fa, 0);
+  store_shared(st0, 0);
+  __syncthreads();
+  for (int it = 0; it < niters; it += 2) {
+    if (it + 1 < niters) {
+      load_shared(it + 1);
+      load_w(fb, it + 1);
+    }
+    compute(fa, st0);
+    if (it + 1 >= niters) break;
+    store_shared(st1, it + 1);
+    __syncthreads();
+    if (it + 2 < niters) {
+      load_shared(it + 2);
+      load_w(fa, it + 2);
+    }
+    compute(fb, st1);
+    if (it + 2 >= niters) break;
+    store_shared(st0, it + 2);
+    __syncthreads();
+  }
+
+  // ---- per block: sum the k-parts (every lane then holds all NR x 4 results
+  // of its row j) and store ----------------------------------------------------
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t rb = row0 + 4 * b;
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[b][rs][r] = kpart_sum(acc[b][rs][r]);
+
+    // lane (kp, j) writes token row r = kp % 4 of row-sets kp / 4 + 4 t
+    const int r = kp & 3;
+    auto pick = [&](int rs) -> float {
+      float v = acc[b][rs][0];
+      v = (r == 1) ? acc[b][rs][1] : v;
+      v = (r == 2) ? acc[b][rs][2] : v;
+      v = (r == 3) ? acc[b][rs][3] : v;
+      return v;
+    };
+    if (PHASE == kGateUp) {
+#pragma unroll
+      for (int t = 0; t < (NR / 2 + 3) / 4; ++t) {
+        const int rsg = (kp >> 2) + 4 * t;
+        if (rsg >= NR / 2) continue;
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int rs = 0; rs < NR / 2; ++rs) {
+          if (rs == rsg) {
+            g = pick(rs);
+            u = pick(rs + NR / 2);
+          }
+        }
+        const int col = slice * (2 * NR) + 4 * rsg + j;
+        const uint16_t hb = (uint16_t)(pack_bf16x2(silu_mul(g, u), 0.f) & 0xFFFFu);
+        if (INT4) {
+          p.h_routed[(rb + r) * p.I + col] = hb;
+        } else if (rb + r < p.T) {
+          p.h_shared[(rb + r) * p.I + col] = hb;
+        }
+      }
+    } else {
+      float* dst = nullptr;
+      if (INT4) {
+        const int32_t pair = p.sorted_ids[rb + r];
+        if (pair < p.P) dst = p.y_routed + (int64_t)pair * p.N;
+      } else if (rb + r < p.T) {
+        dst = p.y_shared + (rb + r) * p.N;
+      }
+#pragma unroll
+      for (int t = 0; t < (NR + 3) / 4; ++t) {
+        const int rsd = (kp >> 2) + 4 * t;
+        if (rsd >= NR) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs)
+          if (rs == rsd) v = pick(rs);
+        if (dst) dst[slice * (4 * NR) + 4 * rsd + j] = v;
+      }
+    }
+  }
+}
+
+// One work-group = one block of rows x 4 consecutive wave slices, numbered
+// block-major (consecutive work-groups stream consecutive rows of one expert;
+// the default round-robin placement then spreads them over the XCDs). Routed
+// work-groups first (4-row blocks), then the shared expert's (kTokBlocks
+// 4-token blocks per work-group).
+template <int PHASE, int NR, int NRS>
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void small_gemm_kernel(GemmParams p) {
+  constexpr int kLds = 2 * (stage_bytes<NR, true, 1>() > stage_bytes<NRS, false, kTokBlocks>()
+                                ? stage_bytes<NR, true, 1>()
+                                : stage_bytes<NRS, false, kTokBlocks>());
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  const int wg_slices = p.N / slice_cols<PHASE, NR>() / kWaves;
+  const int64_t bid = blockIdx.x;
+  const int64_t routed = (int64_t)p.max_blocks * wg_slices;
+  if (bid < routed) {
+    const int64_t blk = bid / wg_slices;
+    const int s = (int)(bid - blk * wg_slices);
+    if (blk * 4 >= *p.n_padded) return;
+    small_tile<PHASE, NR, true, 1>(p, blk * 4, s * kWaves, lds);
+  } else {
+    const int ns = p.N / slice_cols<PHASE, NRS>() / kWaves;
+    const int64_t b2 = bid - routed;
+    const int64_t tg = b2 / ns;
+    const int s = (int)(b2 - tg * ns);
+    if (p.wshared == nullptr) return;
+    small_tile<PHASE, NRS, false, kTokBlocks>(p, tg * 4 * kTokBlocks, s * kWaves, lds);
+  }
+}
+
+template <int PHASE, int NR, int NRS>
+hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
+  // every work-group holds whole 4-slice groups: N must split evenly
+  if (p.N % (slice_cols<PHASE, NR>() * kWaves) || p.N % (slice_cols<PHASE, NRS>() * kWaves))
+    return hipErrorInvalidValue;
+  const int64_t routed = (int64_t)p.max_blocks * (p.N / slice_cols<PHASE, NR>() / kWaves);
+  const int64_t shared = p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) *
+                                         (p.N / slice_cols<PHASE, NRS>() / kWaves)
+                                   : 0;
+  const int64_t grid = routed + shared;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  GemmParams args = p;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS>),
+                         dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream) {
+  return launch_small<kGateUp, kNR, kNRS>(p, stream);
+}
+
+hipError_t launch_down_small(const GemmParams& p, hipStream_t stream) {
+  return launch_small<kDown, kNR, kNRS>(p, stream);
+}
+
+}  // namespace moe

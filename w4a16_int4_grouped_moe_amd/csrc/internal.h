@@ -44,6 +44,10 @@ struct GemmParams {
 hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stream);
 hipError_t launch_down(const GemmParams& p, int32_t block_m, hipStream_t stream);
 
+// Small-batch variants (buckets padded to 4 rows; see gemm_small.hip).
+hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream);
+hipError_t launch_down_small(const GemmParams& p, hipStream_t stream);
+
 // out[t] = bf16(s[t] + sum_j valid * w[t,j] * y[t*k+j]), fp32 sum in slot order.
 hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
                           const float* topk_weights, uint16_t* out, int64_t T, int32_t H,
