@@ -45,6 +45,7 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
   const int64_t P = p->num_tokens * p->top_k;
   const int64_t E = p->num_experts;
   if (P <= 4 * E) return 4;
+  if (P >= 64 * E && p->hidden % 256 == 0) return 128;
   return P >= 32 * E ? 64 : 16;
 }
 
@@ -180,6 +181,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.P = T * k;
   g.k = k;
   g.I = I;
+  g.nibble_mask = 0x0F0F0F0Fu;
 
   // gate_up + SwiGLU
   g.a_routed = static_cast<const uint16_t*>(x);

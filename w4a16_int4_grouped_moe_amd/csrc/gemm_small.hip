@@ -432,30 +432,32 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 
 // One work-group = one block of rows x 4 consecutive wave slices, numbered
 // block-major (consecutive work-groups stream consecutive rows of one expert;
-// the default round-robin placement then spreads them over the XCDs). Routed
-// work-groups first (4-row blocks), then the shared expert's (kTokBlocks
-// 4-token blocks per work-group).
+// the default round-robin placement then spreads them over the XCDs). The
+// shared expert's work-groups (kTokBlocks 4-token blocks each) come first:
+// each streams twice the bytes of a routed one (bf16 weights), so starting
+// them first keeps them out of the kernel's tail. Routed work-groups (one
+// 4-row bucket block each) follow.
 template <int PHASE, int NR, int NRS>
 __global__ __launch_bounds__(kThreads, kWavesPerSimd) void small_gemm_kernel(GemmParams p) {
   constexpr int kLds = 2 * (stage_bytes<NR, true, 1>() > stage_bytes<NRS, false, kTokBlocks>()
                                 ? stage_bytes<NR, true, 1>()
                                 : stage_bytes<NRS, false, kTokBlocks>());
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
-  const int wg_slices = p.N / slice_cols<PHASE, NR>() / kWaves;
   const int64_t bid = blockIdx.x;
-  const int64_t routed = (int64_t)p.max_blocks * wg_slices;
-  if (bid < routed) {
-    const int64_t blk = bid / wg_slices;
-    const int s = (int)(bid - blk * wg_slices);
+  const int ns = p.N / slice_cols<PHASE, NRS>() / kWaves;
+  const int64_t shared =
+      p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) * ns : 0;
+  if (bid < shared) {
+    const int64_t tg = bid / ns;
+    const int s = (int)(bid - tg * ns);
+    small_tile<PHASE, NRS, false, kTokBlocks>(p, tg * 4 * kTokBlocks, s * kWaves, lds);
+  } else {
+    const int wg_slices = p.N / slice_cols<PHASE, NR>() / kWaves;
+    const int64_t b2 = bid - shared;
+    const int64_t blk = b2 / wg_slices;
+    const int s = (int)(b2 - blk * wg_slices);
     if (blk * 4 >= *p.n_padded) return;
     small_tile<PHASE, NR, true, 1>(p, blk * 4, s * kWaves, lds);
-  } else {
-    const int ns = p.N / slice_cols<PHASE, NRS>() / kWaves;
-    const int64_t b2 = bid - routed;
-    const int64_t tg = b2 / ns;
-    const int s = (int)(b2 - tg * ns);
-    if (p.wshared == nullptr) return;
-    small_tile<PHASE, NRS, false, kTokBlocks>(p, tg * 4 * kTokBlocks, s * kWaves, lds);
   }
 }
 

@@ -39,6 +39,7 @@ struct GemmParams {
   int32_t K;                    // reduction width (H for gate_up, I for down)
   int32_t I;                    // intermediate width
   int32_t N;                    // output width (I for gate_up, H for down)
+  uint32_t nibble_mask;         // 0x0F0F0F0F (a run-time value on purpose)
 };
 
 hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stream);
