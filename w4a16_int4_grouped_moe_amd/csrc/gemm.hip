@@ -91,6 +91,11 @@ constexpr int tile_cols() {  // output columns of one work-group
 constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 constexpr uint32_t kNoRow = 0x80000000u;   // buffer offset past any tensor: loads 0
 
+// A wave-uniform byte offset for the scalar offset field of a buffer load;
+// readfirstlane makes it an SGPR value, so the compiler emits one load instead
+// of a loop over distinct lane values.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // One work-group tile. INT4 selects the routed (int4 + scales) or the shared
 // (bf16) weight format.
 template <int BM, int PHASE, int NSUB, bool INT4>
@@ -192,16 +197,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int mblk, int til
   auto load_chunk = [&](int ch) {
 #pragma unroll
     for (int i = 0; i < kLoadsA; ++i)
-      a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[i], ch * kBK * 2, 0);
+      a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[i], uniform(ch * kBK * 2), 0);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if (INT4) {
-        bq_reg[s][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], ch * 64, 0);
-        sc_reg[s] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[s], ch * 8, 0);
+        bq_reg[s][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], uniform(ch * 64), 0);
+        sc_reg[s] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[s], uniform(ch * 8), 0);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bq_reg[s][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s] + 16 * j, ch * kBK * 2, 0);
+          bq_reg[s][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s] + 16 * j, uniform(ch * kBK * 2), 0);
       }
     }
   };
@@ -294,7 +299,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int mblk, int til
 }
 
 // Work-groups: routed (max_blocks x tiles of NSUB sub-tiles per wave) first,
-// then the shared expert's (row blocks of BM tokens x tiles of NSUBS).
+// then the shared expert's (row blocks of BM tokens x tiles of NSUBS), both
+// block-major. (Remapping work-group ids so that each XCD runs a contiguous
+// range of items was measured slower on MI355X than the default round-robin
+// placement, for this kernel and for the small-batch one.)
 template <int BM, int PHASE, int NSUB, int NSUBS>
 __global__ __launch_bounds__(kThreads, BM >= 128 ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLdsRow];

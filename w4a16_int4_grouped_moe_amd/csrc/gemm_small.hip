@@ -60,6 +60,11 @@ constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
 constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 constexpr int kXBytes = 4 * 64 * 16;       // activation fragments per iteration
 
+// A wave-uniform byte offset for the scalar offset field of a buffer load;
+// readfirstlane makes it an SGPR value, so the compiler emits one load instead
+// of a loop over distinct lane values.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 enum { kGateUp = 0, kDown = 1 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
@@ -217,12 +222,12 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) {
       if (INT4) {
-        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], it * (kGroupsPerIt * 16), 0);
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], uniform(it * (kGroupsPerIt * 16)), 0);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           f.w[rs][q] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs] + 16 * q,
-                                                             it * (kGroupsPerIt * 64), 0);
+                                                             uniform(it * (kGroupsPerIt * 64)), 0);
       }
     }
     if (tail && it == niters - 1) {  // groups past the end of K contribute zero
@@ -242,9 +247,9 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
   auto load_shared = [&](int it) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      xs_reg[b] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[b], it * (kGroupsPerIt * 64), 0);
+      xs_reg[b] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[b], uniform(it * (kGroupsPerIt * 64)), 0);
     if (st_active)
-      sc_reg = __builtin_amdgcn_raw_buffer_load_b128(sres, soff, it * (kGroupsPerIt * 2), 0);
+      sc_reg = __builtin_amdgcn_raw_buffer_load_b128(sres, soff, uniform(it * (kGroupsPerIt * 2)), 0);
   };
   auto store_shared = [&](uint8_t* stage, int it) {
 #pragma unroll
