@@ -53,7 +53,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kNR = MOE_SMALL_NR;
 constexpr int kWavesPerSimd = kNR >= 8 ? 2 : 4;  // occupancy target
 constexpr int kNRS = 2;        // bf16 shared-expert row-sets per wave
-constexpr int kTokBlocks = kNR >= 8 ? 4 : 2;  // 4-token blocks per shared-expert work-group
+constexpr int kTokBlocks = kNR >= 8 ? 4 : (kNR >= 4 ? 2 : 1);  // 4-token blocks per shared-expert work-group
 constexpr int kGroupsPerIt = 16;  // k-parts = MFMA blocks
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
 constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
