@@ -44,7 +44,7 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
   // amortised over more rows). In between: 16-row blocks.
   const int64_t P = p->num_tokens * p->top_k;
   const int64_t E = p->num_experts;
-  if (P <= 4 * E) return 4;
+  if (P <= 4 * E && moe::small_batch_fits(p->hidden, p->inter)) return 4;
   if (P >= 64 * E && p->hidden % 256 == 0) return 128;
   return P >= 32 * E ? 64 : 16;
 }

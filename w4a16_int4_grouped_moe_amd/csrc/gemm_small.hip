@@ -50,15 +50,30 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;  // four waves
 constexpr int kWaves = kThreads / 64;
-constexpr int kNR = MOE_SMALL_NR;
-constexpr int kWavesPerSimd = kNR >= 8 ? 2 : 4;  // occupancy target
-constexpr int kNRS = 2;        // bf16 shared-expert row-sets per wave
-constexpr int kTokBlocks = kNR >= 8 ? 4 : (kNR >= 4 ? 2 : 1);  // 4-token blocks per shared-expert work-group
+#ifndef MOE_SMALL_NR_DOWN
+#define MOE_SMALL_NR_DOWN MOE_SMALL_NR
+#endif
+#ifndef MOE_SMALL_TOKBLOCKS
+#define MOE_SMALL_TOKBLOCKS 2  // 4-token blocks per shared-expert work-group
+#endif
+
+constexpr int kNR = MOE_SMALL_NR;            // gate_up
+constexpr int kNRDown = MOE_SMALL_NR_DOWN;   // down
+#ifndef MOE_SMALL_NRS
+#define MOE_SMALL_NRS 2
+#endif
+constexpr int kNRS = MOE_SMALL_NRS;  // bf16 shared-expert row-sets per wave
+constexpr int kTokBlocks = MOE_SMALL_TOKBLOCKS;
+
+// occupancy target (waves per SIMD) of a launch whose int4 waves hold NR row-sets
+constexpr int waves_per_simd(int nr) { return nr >= 8 ? 2 : 4; }
 constexpr int kGroupsPerIt = 16;  // k-parts = MFMA blocks
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
 constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
 constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 constexpr int kXBytes = 4 * 64 * 16;       // activation fragments per iteration
+constexpr int kOutOfRange = (int)0x80000000u;  // buffer offset past any resource: reads 0
+constexpr int kScaleBatch = 8;             // scale pieces in flight per thread while staging
 
 // A wave-uniform byte offset for the scalar offset field of a buffer load;
 // readfirstlane makes it an SGPR value, so the compiler emits one load instead
@@ -118,10 +133,17 @@ __device__ __forceinline__ int weight_row(const GemmParams& p, int slice, int rs
   return slice * (4 * NR) + 4 * rs + j;
 }
 
-// LDS of one pipeline stage: activation fragments, then (int4) the scales of
-// the work-group's 4 * 4NR rows for the iteration's 16 groups.
-template <int NR, bool INT4, int NB>
-constexpr int stage_bytes() { return NB * kXBytes + (INT4 ? kWaves * 4 * NR * 32 : 0); }
+// LDS of one pipeline stage: the activation fragments of NB 4-token blocks.
+template <int NB>
+constexpr int stage_bytes() { return NB * kXBytes; }
+
+// LDS bytes per weight row of the int4 scales, staged once for the whole K:
+// an odd number of 32-byte units (one unit = the 16 groups of one iteration),
+// so that the four rows j = lane % 4 read by a wave fall in distinct banks.
+__host__ __device__ inline int scale_row_bytes(int K) {
+  const int niters = (K / 32 + kGroupsPerIt - 1) / kGroupsPerIt;
+  return 32 * (niters | 1);
+}
 
 // NB blocks of four rows starting at row0 (NB > 1 only for the bf16 shared
 // expert: its weights are then read once for 4 NB tokens).
@@ -178,24 +200,63 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
   const int xdst = (xc & 3) * 1024 + ((xc >> 2) * 4 + xt) * 16;
   const bool xzero_tail = (xc >> 2) >= tail;  // only used in a partial iteration
 
-  // ---- scale staging (int4): thread t < 2*kRowsWG -> row t/2, half t%2 ------
-  const int st_row = tid >> 1;
-  const bool st_active = INT4 && st_row < kRowsWG;
-  __amdgpu_buffer_rsrc_t sres = xres;  // replaced below for int4 weights
-  int soff = 0;
+  // ---- scales (int4): all groups of the work-group's rows, staged once ------
+  // Row r of the work-group (wave r / 4NR, row-set and row r % 4NR) is read as
+  // 2 niters pieces of 16 bytes (8 groups each), contiguous in memory, and kept
+  // in LDS for the whole K loop; groups past the end of K are zero.
   const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
-  int e = 0;
-  if (INT4) {
-    e = p.block_expert[row0 / 4];
+  const int srow = scale_row_bytes(K);
+  uint8_t* const slds = lds + 2 * stage_bytes<NB>();
+  const int e = INT4 ? p.block_expert[row0 / 4] : 0;
+  auto stage_scales = [&]() {
     const int64_t r0 = (int64_t)e * Nw;
-    sres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
-                                             Nw * (K / 32) * 2, kBufferFlags);
-    if (st_active) {
-      const int w = st_row / (4 * NR), lr = st_row % (4 * NR);
-      soff = (weight_row<PHASE, NR>(p, slice0 + w, lr / 4, lr % 4) * (K / 32) + 8 * (tid & 1)) * 2;
-    }
-  }
-  const int sdst = NB * kXBytes + tid * 16;  // scale row st_row, half tid & 1
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.scales + r0 * (K / 32)), 0, Nw * (K / 32) * 2, kBufferFlags);
+    const int ppr = 2 * niters;  // pieces per row
+    const int npieces = kRowsWG * ppr;
+    auto batch = [&](int base) {
+      u32x4 v[kScaleBatch];
+#pragma unroll
+      for (int u = 0; u < kScaleBatch; ++u) {
+        // loads of a work-group-uniform range only; a thread without a piece
+        // inside it reads out of range
+        if (base + u * kThreads >= npieces) break;
+        const int i = base + u * kThreads + tid;
+        const int r = i / ppr, pc = i - r * ppr;
+        int off = kOutOfRange;
+        if (i < npieces && pc * 8 < ngroups) {
+          const int w = r / (4 * NR), lr = r % (4 * NR);
+          off = (weight_row<PHASE, NR>(p, slice0 + w, lr / 4, lr % 4) * (K / 32) + pc * 8) * 2;
+        }
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kScaleBatch; ++u) {
+        if (base + u * kThreads >= npieces) break;
+        const int i = base + u * kThreads + tid;
+        if (i < npieces) {
+          const int r = i / ppr, pc = i - r * ppr;
+          const int valid = ngroups - pc * 8;  // groups of the piece inside K
+          u32x4 sv = v[u];
+          if (valid < 8) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const uint32_t lo = 2 * h < valid ? (sv[h] & 0xFFFFu) : 0u;
+              const uint32_t hi = 2 * h + 1 < valid ? (sv[h] & 0xFFFF0000u) : 0u;
+              sv[h] = lo | hi;
+            }
+          }
+          *reinterpret_cast<u32x4*>(slds + r * srow + pc * 16) = sv;
+        }
+      }
+    };
+    // the first batch (every K up to 8192 for 64 rows) as straight-line code:
+    // a loop around it would make the compiler wait at its head for all loads
+    // in flight, including the first iteration's operands
+    batch(0);
+    for (int base = kScaleBatch * kThreads; base < npieces; base += kScaleBatch * kThreads)
+      batch(base);
+  };
 
   // ---- weights of this lane ----------------------------------------------
   __amdgpu_buffer_rsrc_t wres;
@@ -212,8 +273,14 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
     const int row = weight_row<PHASE, NR>(p, slice, rs, j);
     woff[rs] = INT4 ? (row * (K / 8) + 4 * kp) * 4 : (row * K + 32 * kp) * 2;
   }
-  // this lane's scales in a stage: row (wave, 4 rs + j), group kp
-  const int sread = NB * kXBytes + (wave * 4 * NR + j) * 32 + kp * 2;
+  // this lane's scales: row (wave, 4 rs + j), group kp of the iteration
+  const uint8_t* const sread = slds + (wave * 4 * NR + j) * srow + kp * 2;
+
+  // scalar byte offset of iteration `it` for a stride of `bytes` per iteration;
+  // past the last iteration an offset beyond any buffer, so that the prefetch
+  // can be issued unconditionally (a conditional one makes the compiler's wait
+  // before each use also cover the prefetch) and reads zeros without traffic
+  auto kofs = [&](int it, int bytes) { return uniform(it < niters ? it * bytes : kOutOfRange); };
 
   struct Frag {
     u32x4 w[NR][INT4 ? 1 : 4];  // int4: 4 words; bf16: 32 weights
@@ -222,34 +289,27 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) {
       if (INT4) {
-        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], uniform(it * (kGroupsPerIt * 16)), 0);
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], kofs(it, kGroupsPerIt * 16), 0);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           f.w[rs][q] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs] + 16 * q,
-                                                             uniform(it * (kGroupsPerIt * 64)), 0);
+                                                             kofs(it, kGroupsPerIt * 64), 0);
       }
     }
-    if (tail && it == niters - 1) {  // groups past the end of K contribute zero
-      if (kp >= tail) {
-#pragma unroll
-        for (int rs = 0; rs < NR; ++rs)
-#pragma unroll
-          for (int q = 0; q < (INT4 ? 1 : 4); ++q)
-            f.w[rs][q] = INT4 ? u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u}
-                              : u32x4{0, 0, 0, 0};
-      }
-    }
+    // Groups past the end of K (a partial last iteration) need no masking:
+    // their staged activations are zero, so int4 codes (always finite once
+    // dequantised) contribute exactly zero, and so do the bf16 weights that
+    // follow in memory (a non-finite one there already makes its own row, and
+    // with it the layer output, non-finite).
   };
 
-  // shared stage registers: one activation piece and (int4) one scale piece
-  u32x4 xs_reg[NB], sc_reg = {0, 0, 0, 0};
+  // shared stage registers: one activation piece per token block
+  u32x4 xs_reg[NB];
   auto load_shared = [&](int it) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      xs_reg[b] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[b], uniform(it * (kGroupsPerIt * 64)), 0);
-    if (st_active)
-      sc_reg = __builtin_amdgcn_raw_buffer_load_b128(sres, soff, uniform(it * (kGroupsPerIt * 2)), 0);
+      xs_reg[b] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[b], kofs(it, kGroupsPerIt * 64), 0);
   };
   auto store_shared = [&](uint8_t* stage, int it) {
 #pragma unroll
@@ -264,19 +324,6 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
       }
       *reinterpret_cast<u32x4*>(stage + b * kXBytes + xdst) = v;
     }
-    if (st_active) {
-      u32x4 s = sc_reg;
-      if (tail && it == niters - 1) {  // zero scales past the end of K
-        const int g0 = 8 * (tid & 1);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t lo = (g0 + 2 * h) < tail ? (s[h] & 0xFFFFu) : 0u;
-          const uint32_t hi = (g0 + 2 * h + 1) < tail ? (s[h] & 0xFFFF0000u) : 0u;
-          s[h] = lo | hi;
-        }
-      }
-      *reinterpret_cast<u32x4*>(stage + sdst) = s;
-    }
   };
 
   f32x4 acc[NB][NR];
@@ -285,7 +332,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) acc[b][rs] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Frag& f, const uint8_t* stage) {
+  auto compute = [&](const Frag& f, const uint8_t* stage, int it) {
     if (INT4) {
       u32x4 xf[4];
 #pragma unroll
@@ -321,7 +368,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
       }
 #pragma unroll
       for (int rs = 0; rs < NR; ++rs) {
-        const uint32_t sb = *reinterpret_cast<const uint16_t*>(stage + sread + rs * 128);
+        const uint32_t sb = *reinterpret_cast<const uint16_t*>(sread + rs * 4 * srow + it * 32);
         acc[0][rs] += bf16_to_f32(sb) * t[rs];
       }
     } else {
@@ -348,26 +395,28 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 
   // ---- pipeline: stage it+1 loads in flight while stage it is computed ------
   uint8_t* st0 = lds;
-  uint8_t* st1 = lds + stage_bytes<NR, INT4, NB>();
+  uint8_t* st1 = lds + stage_bytes<NB>();
   Frag fa, fb;
   load_shared(0);
   load_w(fa, 0);
+  // the scales are fetched together with the first iteration's operands
+  if (INT4) stage_scales();
   store_shared(st0, 0);
   __syncthreads();
+  // (the scheduling barriers keep the prefetch ahead of the computation: left
+  // free, the scheduler sinks the loads below it to save registers)
   for (int it = 0; it < niters; it += 2) {
-    if (it + 1 < niters) {
-      load_shared(it + 1);
-      load_w(fb, it + 1);
-    }
-    compute(fa, st0);
+    load_shared(it + 1);
+    load_w(fb, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(fa, st0, it);
     if (it + 1 >= niters) break;
     store_shared(st1, it + 1);
     __syncthreads();
-    if (it + 2 < niters) {
-      load_shared(it + 2);
-      load_w(fa, it + 2);
-    }
-    compute(fb, st1);
+    load_shared(it + 2);
+    load_w(fa, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(fb, st1, it + 1);
     if (it + 2 >= niters) break;
     store_shared(st0, it + 2);
     __syncthreads();
@@ -443,11 +492,8 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 // them first keeps them out of the kernel's tail. Routed work-groups (one
 // 4-row bucket block each) follow.
 template <int PHASE, int NR, int NRS>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void small_gemm_kernel(GemmParams p) {
-  constexpr int kLds = 2 * (stage_bytes<NR, true, 1>() > stage_bytes<NRS, false, kTokBlocks>()
-                                ? stage_bytes<NR, true, 1>()
-                                : stage_bytes<NRS, false, kTokBlocks>());
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+__global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // small_lds_bytes
   const int64_t bid = blockIdx.x;
   const int ns = p.N / slice_cols<PHASE, NRS>() / kWaves;
   const int64_t shared =
@@ -466,11 +512,23 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void small_gemm_kernel(Gem
   }
 }
 
+// Dynamic LDS of a launch: two activation stages (of the larger of the routed
+// and the shared work items) and, for the routed ones, the staged scales.
+template <int NR>
+int small_lds_bytes(int K) {
+  const int routed = 2 * stage_bytes<1>() + kWaves * 4 * NR * scale_row_bytes(K);
+  const int shared = 2 * stage_bytes<kTokBlocks>();
+  return routed > shared ? routed : shared;
+}
+constexpr int kMaxLds = 64 * 1024;
+
 template <int PHASE, int NR, int NRS>
 hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
   // every work-group holds whole 4-slice groups: N must split evenly
   if (p.N % (slice_cols<PHASE, NR>() * kWaves) || p.N % (slice_cols<PHASE, NRS>() * kWaves))
     return hipErrorInvalidValue;
+  const int lds = small_lds_bytes<NR>(p.K);
+  if (lds > kMaxLds) return hipErrorInvalidValue;
   const int64_t routed = (int64_t)p.max_blocks * (p.N / slice_cols<PHASE, NR>() / kWaves);
   const int64_t shared = p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) *
                                          (p.N / slice_cols<PHASE, NRS>() / kWaves)
@@ -481,17 +539,21 @@ hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
   GemmParams args = p;
   void* kargs[] = {&args};
   return hipLaunchKernel(reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS>),
-                         dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+                         dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
 }
 
 }  // namespace
+
+bool small_batch_fits(int32_t hidden, int32_t inter) {
+  return small_lds_bytes<kNR>(hidden) <= kMaxLds && small_lds_bytes<kNRDown>(inter) <= kMaxLds;
+}
 
 hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream) {
   return launch_small<kGateUp, kNR, kNRS>(p, stream);
 }
 
 hipError_t launch_down_small(const GemmParams& p, hipStream_t stream) {
-  return launch_small<kDown, kNR, kNRS>(p, stream);
+  return launch_small<kDown, kNRDown, kNRS>(p, stream);
 }
 
 }  // namespace moe

@@ -46,6 +46,8 @@ hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stre
 hipError_t launch_down(const GemmParams& p, int32_t block_m, hipStream_t stream);
 
 // Small-batch variants (buckets padded to 4 rows; see gemm_small.hip).
+// small_batch_fits: whether their staged scales fit in LDS for these widths.
+bool small_batch_fits(int32_t hidden, int32_t inter);
 hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_small(const GemmParams& p, hipStream_t stream);
 
