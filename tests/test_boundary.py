@@ -61,7 +61,7 @@ def test_workspace_size_and_block_m(lib):
     p = P()
     assert moe.forward_block_m(p) == 4
     assert moe.forward_block_m(P(num_tokens=512)) == 16
-    assert moe.forward_block_m(P(num_tokens=4096)) == 128
+    assert moe.forward_block_m(P(num_tokens=4096)) == 96
     assert moe.forward_block_m(P(num_tokens=4096, hidden=7040)) == 64  # 7040 % 256 != 0
     assert moe.forward_block_m(P(num_tokens=2048)) == 64
     n = moe.workspace_size(p)

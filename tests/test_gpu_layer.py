@@ -63,6 +63,34 @@ def test_mid_shapes(dev, T, E, k, base, bm_rows):
     check(mi.bf16_tensor_to_f64(out), ref, f"mid T={T} ({bm_rows})")
 
 
+@pytest.mark.parametrize("T,H,I,E,k,base,shared", [
+    (500, 1024, 512, 6, 2, 0, True),     # two column tiles per phase, 2-3 blocks per expert
+    (400, 512, 256, 5, 4, 3, True),      # expert base, non-local and invalid ids
+    (130, 2048, 256, 2, 2, 0, True),     # several scale buffers per block (K = 2048)
+])
+def test_prefill_shapes(dev, T, H, I, E, k, base, shared):
+    """Shapes that take the prefill kernel (many rows per expert, widths that
+    fit its tiles): block row counts from a few rows to full blocks."""
+    import torch
+    import w4a16_int4_grouped_moe_amd as moe
+
+    n_global = base + E + 3
+    bm = moe.forward_block_m(moe.problem(T, H, I, E, k, base))
+    assert bm > 64, bm
+    bank = mi.weight_bank(40 + H, H, I, list(range(base, base + E)))
+    bank_dev = {kk: mi.to_device(v, dev) for kk, v in bank.__dict__.items()}
+    x = mi.activations(41, T, H)
+    ids, w = mi.routing_uniform(42, T, n_global, k)
+    ids[::11, -1] = -1
+    sw = mi.shared_weights(43, H, I) if shared else None
+    print(f"[case] prefill T={T} H={H} I={I} E={E} k={k} base={base} bm={bm}", flush=True)
+    out = run_layer(dev, x, ids, w, bank_dev, sw, expert_base=base)
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw, base)
+    check(mi.bf16_tensor_to_f64(out), ref, f"prefill T={T} H={H} I={I}")
+
+
 # ------------------------------------------------------- Kimi-K2.6 layer shape
 @pytest.fixture(scope="module")
 def kimi(dev):

@@ -40,12 +40,13 @@ int64_t sorted_capacity(const moe_w4a16_problem* p, int32_t bm) {
 
 int32_t choose_block_m(const moe_w4a16_problem* p) {
   // About one row per expert (decode): 4-row buckets and the weight-streaming
-  // small-batch kernels. Many rows per expert: 64-row blocks (dequantisation
-  // amortised over more rows). In between: 16-row blocks.
+  // small-batch kernels. Many rows per expert (prefill): the prefill kernel's
+  // blocks, or 64-row blocks where its tiles do not fit the widths. In
+  // between: 16-row blocks.
   const int64_t P = p->num_tokens * p->top_k;
   const int64_t E = p->num_experts;
   if (P <= 4 * E && moe::small_batch_fits(p->hidden, p->inter)) return 4;
-  if (P >= 64 * E && p->hidden % 256 == 0) return 128;
+  if (P >= 64 * E && moe::prefill_fits(p->hidden, p->inter)) return moe::prefill_block_m();
   return P >= 32 * E ? 64 : 16;
 }
 
@@ -172,6 +173,21 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
                                      n_padded, strm);
   if (err != hipSuccess) return hip_status(err);
 
+  // One GEMM phase. Prefill blocks: the routed experts in the prefill kernel,
+  // the shared expert in a second launch of the tiled kernel (64-token tiles).
+  auto gemm = [&](const moe::GemmParams& gp, bool gate_up) -> hipError_t {
+    if (L.bm == 4)
+      return gate_up ? moe::launch_gate_up_small(gp, strm) : moe::launch_down_small(gp, strm);
+    if (L.bm != moe::prefill_block_m())
+      return gate_up ? moe::launch_gate_up(gp, L.bm, strm) : moe::launch_down(gp, L.bm, strm);
+    hipError_t e = gate_up ? moe::launch_gate_up_prefill(gp, strm)
+                           : moe::launch_down_prefill(gp, strm);
+    if (e != hipSuccess || !gp.wshared) return e;
+    moe::GemmParams gs = gp;
+    gs.max_blocks = 0;  // shared-expert tiles only
+    return gate_up ? moe::launch_gate_up(gs, 64, strm) : moe::launch_down(gs, 64, strm);
+  };
+
   moe::GemmParams g{};
   g.sorted_ids = sorted;
   g.block_expert = blk;
@@ -194,7 +210,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.K = H;
   g.N = I;
   if ((err = mark(1)) != hipSuccess) return hip_status(err);
-  err = L.bm == 4 ? moe::launch_gate_up_small(g, strm) : moe::launch_gate_up(g, L.bm, strm);
+  err = gemm(g, true);
   if (err != hipSuccess) return hip_status(err);
 
   // down
@@ -208,7 +224,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.K = I;
   g.N = H;
   if ((err = mark(2)) != hipSuccess) return hip_status(err);
-  err = L.bm == 4 ? moe::launch_down_small(g, strm) : moe::launch_down(g, L.bm, strm);
+  err = gemm(g, false);
   if (err != hipSuccess) return hip_status(err);
 
   if ((err = mark(3)) != hipSuccess) return hip_status(err);

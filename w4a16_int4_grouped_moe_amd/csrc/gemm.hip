@@ -194,19 +194,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int mblk, int til
   u32x4 bq_reg[NSUB][INT4 ? 1 : 4];  // int4: four words (one group); bf16: 32 weights
   uint32_t sc_reg[NSUB];             // int4: scale bits
 
+  // Chunk ch's loads. Past the last chunk the scalar offset lies beyond every
+  // buffer (the loads return zeros without traffic), so that the prefetch is
+  // issued unconditionally: a conditional one makes the compiler's wait
+  // before each use also cover the loads just issued.
+  auto cofs = [&](int ch, int bytes) { return uniform(ch < nchunks ? ch * bytes : (int)kNoRow); };
   auto load_chunk = [&](int ch) {
 #pragma unroll
     for (int i = 0; i < kLoadsA; ++i)
-      a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[i], uniform(ch * kBK * 2), 0);
+      a_reg[i] = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[i], cofs(ch, kBK * 2), 0);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if (INT4) {
-        bq_reg[s][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], uniform(ch * 64), 0);
-        sc_reg[s] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[s], uniform(ch * 8), 0);
+        bq_reg[s][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], cofs(ch, 64), 0);
+        sc_reg[s] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[s], cofs(ch, 8), 0);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bq_reg[s][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s] + 16 * j, uniform(ch * kBK * 2), 0);
+          bq_reg[s][j] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s] + 16 * j, cofs(ch, kBK * 2), 0);
       }
     }
   };
@@ -236,7 +241,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int mblk, int til
       n8[s] = -8.0f * sc[s];
     }
     __syncthreads();
-    if (ch + 1 < nchunks) load_chunk(ch + 1);
+    load_chunk(ch + 1);
+    // keep the prefetch ahead of the MFMAs (the scheduler would sink it)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 bw[NSUB];

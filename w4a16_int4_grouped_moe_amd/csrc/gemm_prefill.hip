@@ -1,0 +1,395 @@
+// gemm_prefill.hip -- grouped W4A16 GEMMs for many rows per expert (gfx950):
+// the int4 routed experts of prefill-sized batches, 128-row bucket blocks.
+//
+// Same two launches as the other GEMM paths (gate_up with the SwiGLU epilogue,
+// then down), for blocks of 128 bucketed rows of one expert. Here the layer is
+// a dense contraction per expert (about 85 rows each for 4096 tokens, top-8 of
+// 384), so the kernel is built around keeping the MFMA pipes fed: every
+// dequantised weight serves all rows of the block, and all operands arrive
+// through LDS without holding registers while in flight.
+//
+// Work-group (512 threads = 8 waves): one block of up to kBM bucketed rows x
+// 512 weight rows. Every wave owns four 16-row weight sub-tiles (gate_up: two
+// gate sub-tiles and the two matching up sub-tiles) and computes them for all
+// of the block's rows, so each weight is dequantised exactly once per block.
+// K advances in chunks of 128 inputs (four 32-input groups). All operands reach
+// LDS through 16-byte buffer loads with an LDS destination (no registers held
+// while in flight), so registers hold only accumulators and the fragments of
+// one MFMA step:
+//  * activations: the kBM x 128 chunk, double buffered; a row's 16 pieces of 16
+//    bytes are permuted (piece c of row r at slot c ^ (r & 7)) so that the
+//    fragment reads of 8 rows at one k offset hit 8 distinct bank groups;
+//  * weights: the 512 rows x 64 bytes (four groups of 32 codes) of the chunk,
+//    double buffered, the four groups of row r permuted by (r >> 1) & 3 for the
+//    same reason; lane (r = lane % 16, q = lane / 16) of a wave reads group q of
+//    row r of each of its sub-tiles;
+//  * scales: 16 groups (4 chunks) of each of the 512 rows, two buffers that
+//    alternate every 4 chunks;
+//  * the words are dequantised to bf16 (u - 8) * s and fed to
+//    v_mfma_f32_16x16x32_bf16: MFMA step j of a chunk takes word j of every
+//    lane, so its 32-long reduction covers one 8-input slice of each of the
+//    four groups; the matching activations are read at those offsets.
+// One barrier per chunk: the copies of chunk c + 1 are issued before chunk c is
+// computed and waited for after it. Barriers are raw s_barrier with explicit
+// waits (the fence of __syncthreads() would also wait for the copies just
+// issued). The number of 16-row sub-tiles holding bucket rows (even, after
+// rounding up) is a template parameter of the K loop, so the loop body is
+// straight-line code.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+#ifndef MOE_PREFILL_MAX_SUBTILES
+#define MOE_PREFILL_MAX_SUBTILES 6
+#endif
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxMS = MOE_PREFILL_MAX_SUBTILES;  // 16-row sub-tiles per block
+constexpr int kBM = 16 * kMaxMS;           // bucket rows per block
+constexpr int kNSub = 4;                   // 16-row weight sub-tiles per wave
+constexpr int kBN = kWaves * kNSub * 16;   // weight rows per work-group
+constexpr int kKC = 128;                   // inputs per chunk
+constexpr int kSPeriod = 4;                // chunks per scale buffer
+constexpr int kABytes = kBM * kKC * 2;     // activation chunk in LDS
+constexpr int kWRowBytes = kKC / 2;        // int4 bytes of a weight row per chunk
+constexpr int kWBytes = kBN * kWRowBytes;
+constexpr int kSRowBytes = kSPeriod * 4 * 2;  // scale bytes of one row per buffer
+constexpr int kSBytes = kBN * kSRowBytes;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
+constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
+
+enum { kGateUp = 0, kDown = 1 };
+
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kABytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kABytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_w0[kWBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kWBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kSBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_s1[kSBytes];
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// The eight codes of one word -> eight bf16 weights (u - 8) * s in input order:
+// even fields masked into the four bytes of one register, odd fields into
+// another, one v_cvt_f32_ubyte per code, fma(u, s, -8 s) exact in fp32, one
+// rounding to bf16. `mask` (0x0F0F0F0F) is a run-time value so that the
+// compiler keeps the byte form.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, uint32_t mask, float s, float neg8s) {
+  const uint32_t ev = w & mask;
+  const uint32_t od = (w >> 4) & mask;
+  u32x4 r;
+  r[0] = pack_bf16x2(fmaf((float)(ev & 0xFFu), s, neg8s), fmaf((float)(od & 0xFFu), s, neg8s));
+  r[1] = pack_bf16x2(fmaf((float)((ev >> 8) & 0xFFu), s, neg8s),
+                     fmaf((float)((od >> 8) & 0xFFu), s, neg8s));
+  r[2] = pack_bf16x2(fmaf((float)((ev >> 16) & 0xFFu), s, neg8s),
+                     fmaf((float)((od >> 16) & 0xFFu), s, neg8s));
+  r[3] = pack_bf16x2(fmaf((float)(ev >> 24), s, neg8s), fmaf((float)(od >> 24), s, neg8s));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// s_waitcnt with only the vector-memory counter limited (lgkm and exp left
+// unconstrained), and with both vector-memory and LDS counters at zero.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int PHASE>
+constexpr int tile_cols() { return PHASE == kGateUp ? kBN / 2 : kBN; }
+
+// Weight row of work-group row R = 64 wave + 16 sub-tile + r.
+template <int PHASE>
+__device__ __forceinline__ int weight_row(const GemmParams& p, int tile, int R) {
+  const int w = R >> 6, s = (R >> 4) & 3, r = R & 15;
+  if (PHASE == kGateUp) {
+    const int c = tile * (kBN / 2) + w * 32 + 16 * (s & 1) + r;
+    return s < 2 ? c : p.I + c;  // gate rows, then the matching up rows
+  }
+  return tile * kBN + w * 64 + 16 * s + r;
+}
+
+template <int PHASE, int MS>
+__device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int tile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int K = p.K;
+  const int nch = K / kKC;
+  const int64_t row0 = (int64_t)mblk * kBM;
+  const int e = p.block_expert[mblk];
+  const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
+  const int64_t wbase = (int64_t)e * Nw;
+
+  // ---- activation copies: instruction t covers LDS rows 4t..4t+3 ------------
+  constexpr int kACopies = kBM / 4;                        // per work-group
+  constexpr int kAPerWave = (kACopies + kWaves - 1) / kWaves;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_routed, 0,
+      (int)((PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM) * K * 2), kBufferFlags);
+  uint32_t aoff[kAPerWave];
+#pragma unroll
+  for (int i = 0; i < kAPerWave; ++i) {
+    const int t = kAPerWave * wave + i;
+    const int row = 4 * t + (lane >> 4);
+    const int piece = (lane & 15) ^ (row & 7);
+    int64_t src = -1;
+    if (t < kACopies && row < MS * 16) {
+      if (PHASE == kGateUp) {
+        const int32_t pair = p.sorted_ids[row0 + row];
+        if (pair < p.P) src = pair / p.k;
+      } else {
+        src = row0 + row;
+      }
+    }
+    aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
+  }
+  auto copy_a = [&](uint8_t* dst, int ch) {
+    const int so = uniform(ch < nch ? ch * kKC * 2 : (int)kNoRow);
+#pragma unroll
+    for (int i = 0; i < kAPerWave; ++i) {
+      const int t = kAPerWave * wave + i;
+      if (kACopies % kWaves == 0 || t < kACopies)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + t * 1024), 16, aoff[i], so, 0, 0);
+    }
+  };
+
+  // ---- weight copies: instruction u covers rows 16u..16u+15 (64 B each) ------
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + wbase * (K / 8)), 0, Nw * (K / 8) * 4, kBufferFlags);
+  uint32_t woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int R = 16 * (4 * wave + i) + (lane >> 2);
+    const int g = (lane & 3) ^ ((R >> 1) & 3);
+    woff[i] = (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 8) + 4 * g) * 4);
+  }
+  auto copy_w = [&](uint8_t* dst, int ch) {
+    const int so = uniform(ch < nch ? ch * kWRowBytes : (int)kNoRow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(dst + (4 * wave + i) * 1024), 16,
+                                               woff[i], so, 0, 0);
+  };
+
+  // ---- scale copies: instruction v covers rows 32v..32v+31 (32 B each) -------
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.scales + wbase * (K / 32)), 0, Nw * (K / 32) * 2, kBufferFlags);
+  uint32_t soff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int R = 32 * (2 * wave + i) + (lane >> 1);
+    soff[i] = (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 32) + 8 * (lane & 1)) * 2);
+  }
+  const int nper = (nch + kSPeriod - 1) / kSPeriod;
+  auto copy_s = [&](uint8_t* dst, int per) {
+    const int so = uniform(per < nper ? per * kSRowBytes : (int)kNoRow);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_ptr)(dst + (2 * wave + i) * 1024), 16,
+                                               soff[i], so, 0, 0);
+  };
+
+  // ---- this lane's LDS read offsets -----------------------------------------
+  // weights: row R = 64 wave + 16 s + lr, group lq (permuted slot)
+  const int wread = (wave * 64 + lr) * kWRowBytes + ((lq ^ ((lr >> 1) & 3)) * 16);
+  // scales: row R, group 4 (chunk % 4) + lq
+  const int sread = (wave * 64 + lr) * kSRowBytes + lq * 2;
+  // activations: row 16 mi + lr, piece 4 lq + j (permuted slot)
+  const int aread = lr * (kKC * 2);
+
+  f32x4 acc[MS][kNSub];
+#pragma unroll
+  for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint8_t* abuf, const uint8_t* wbuf, const float (&sc)[kNSub]) {
+    u32x4 w[kNSub];
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s)
+      w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread + s * 16 * kWRowBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8 bw[kNSub];
+#pragma unroll
+      for (int s = 0; s < kNSub; ++s)
+        bw[s] = dequant8(w[s][j], p.nibble_mask, sc[s], -8.0f * sc[s]);
+      const int apiece = ((4 * lq + j) ^ (lr & 7)) * 16;  // inputs 32 lq + 8 j
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apiece);
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s)
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[s], acc[mi][s], 0, 0, 0);
+      }
+      // one step's operands live at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto read_scales = [&](float (&sc)[kNSub], int ch) {
+    const uint8_t* sb = ((ch / kSPeriod) & 1) ? lds_s1 : lds_s0;
+    const int g = (ch % kSPeriod) * 8;  // bytes: 4 groups per chunk
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s)
+      sc[s] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sb + sread + s * 16 * kSRowBytes + g));
+  };
+
+  // ---- pipeline -----------------------------------------------------------
+  copy_w(lds_w0, 0);
+  copy_a(lds_a0, 0);
+  copy_s(lds_s0, 0);
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  // even chunk: buffers 0; its scales are read before the copies are issued
+  auto even_chunk = [&](int ch) {
+    float sc[kNSub];
+    read_scales(sc, ch);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_w(lds_w1, ch + 1);
+    copy_a(lds_a1, ch + 1);
+    const bool new_s = ch % kSPeriod == 0 && ch / kSPeriod + 1 < nper;
+    if (new_s) copy_s(((ch / kSPeriod + 1) & 1) ? lds_s1 : lds_s0, ch / kSPeriod + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(lds_a0, lds_w0, sc);
+    // chunk ch + 1 in LDS (a scale copy may stay in flight); this chunk's LDS
+    // reads done before its buffers are overwritten
+    if (new_s) wait_vm<2>();
+    else wait_vm<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  // odd chunk: buffers 1 (kSPeriod is even: no scale copy starts here)
+  auto odd_chunk = [&](int ch) {
+    float sc[kNSub];
+    read_scales(sc, ch);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_w(lds_w0, ch + 1);
+    copy_a(lds_a0, ch + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(lds_a1, lds_w1, sc);
+    wait_vm<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  // whole pairs (the chunk count is even; a loop with a second exit between
+  // the halves makes the register allocator move the accumulators)
+  for (int ch = 0; ch < nch; ch += 2) {
+    even_chunk(ch);
+    odd_chunk(ch + 1);
+  }
+
+  // ---- epilogue: lane holds rows 4 lq + i of each 16-row sub-tile, column lr
+  if (PHASE == kGateUp) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int col = tile * (kBN / 2) + wave * 32 + 16 * s + lr;
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t r = row0 + mi * 16 + 4 * lq + i;
+          const float hv = silu_mul(acc[mi][s][i], acc[mi][s + 2][i]);
+          p.h_routed[r * p.I + col] = (uint16_t)(pack_bf16x2(hv, 0.f) & 0xFFFFu);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = row0 + mi * 16 + 4 * lq + i;
+        const int32_t pair = p.sorted_ids[r];
+        if (pair >= p.P) continue;
+        float* dst = p.y_routed + (int64_t)pair * p.N + tile * kBN + wave * 64 + lr;
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s) dst[16 * s] = acc[mi][s][i];
+      }
+  }
+}
+
+// Work-groups: max_blocks x tiles, block-major (the default round-robin
+// placement spreads a block's tiles over the XCDs).
+template <int PHASE>
+__global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p) {
+  const int n_tiles = p.N / tile_cols<PHASE>();
+  const int mblk = blockIdx.x / n_tiles;
+  const int tile = blockIdx.x - mblk * n_tiles;
+  if ((int64_t)mblk * kBM >= *p.n_padded) return;
+  // bucket rows of the block (padding sits at its end), in 16-row sub-tiles
+  const int64_t row0 = (int64_t)mblk * kBM;
+  const int lane = threadIdx.x & 63;
+  int n_valid = 0;
+#pragma unroll
+  for (int h = 0; h < (kBM + 63) / 64; ++h) {
+    const int r = 64 * h + lane;
+    n_valid += __popcll(__ballot(r < kBM && p.sorted_ids[row0 + r] < p.P));
+  }
+  const int msub = uniform((n_valid + 15) >> 4);
+  if (msub <= 2) block_tile<PHASE, 2>(p, mblk, tile);
+  else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4)>(p, mblk, tile);
+  else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6)>(p, mblk, tile);
+  else block_tile<PHASE, kMaxMS>(p, mblk, tile);
+}
+
+template <int PHASE>
+hipError_t launch(const GemmParams& p, hipStream_t stream) {
+  if (p.N % tile_cols<PHASE>() != 0 || p.K % (2 * kKC) != 0) return hipErrorInvalidValue;
+  // buffer resources hold 32-bit byte sizes
+  const int64_t arows = PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM;
+  const int64_t nw = PHASE == kGateUp ? 2 * (int64_t)p.I : p.N;
+  if (arows * p.K * 2 > 0x7fffffff || nw * p.K / 2 > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.max_blocks * (p.N / tile_cols<PHASE>());
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  GemmParams args = p;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE>),
+                         dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+}
+
+}  // namespace
+
+int32_t prefill_block_m() { return kBM; }
+
+bool prefill_fits(int32_t hidden, int32_t inter) {
+  return inter % tile_cols<kGateUp>() == 0 && hidden % tile_cols<kDown>() == 0 &&
+         hidden % (2 * kKC) == 0 && inter % (2 * kKC) == 0;
+}
+
+hipError_t launch_gate_up_prefill(const GemmParams& p, hipStream_t stream) {
+  return launch<kGateUp>(p, stream);
+}
+
+hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream) {
+  return launch<kDown>(p, stream);
+}
+
+}  // namespace moe

@@ -51,6 +51,13 @@ bool small_batch_fits(int32_t hidden, int32_t inter);
 hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_small(const GemmParams& p, hipStream_t stream);
 
+// Routed int4 experts in 128-row blocks (prefill-sized batches; see
+// gemm_prefill.hip). prefill_fits: whether the widths suit its tiles.
+bool prefill_fits(int32_t hidden, int32_t inter);
+int32_t prefill_block_m();  // bucket rows per block of that path
+hipError_t launch_gate_up_prefill(const GemmParams& p, hipStream_t stream);
+hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream);
+
 // out[t] = bf16(s[t] + sum_j valid * w[t,j] * y[t*k+j]), fp32 sum in slot order.
 hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
                           const float* topk_weights, uint16_t* out, int64_t T, int32_t H,
