@@ -17,18 +17,22 @@
 // while in flight), so registers hold only accumulators and the fragments of
 // one MFMA step:
 //  * activations: the kBM x 128 chunk, double buffered; a row's 16 pieces of 16
-//    bytes are permuted (piece c of row r at slot c ^ (r & 7)) so that the
-//    fragment reads of 8 rows at one k offset hit 8 distinct bank groups;
+//    bytes are permuted, piece c of row r at slot c ^ f(r & 15) where f swaps
+//    the two 2-bit halves of its argument, so that the fragment reads (16 rows
+//    at one k offset per 16 lanes) are free of bank conflicts;
 //  * weights: the 512 rows x 64 bytes (four groups of 32 codes) of the chunk,
 //    double buffered, the four groups of row r permuted by (r >> 1) & 3 for the
 //    same reason; lane (r = lane % 16, q = lane / 16) of a wave reads group q of
 //    row r of each of its sub-tiles;
+//    (both permutations measured free of bank conflicts on gfx950 16-byte LDS
+//    reads, where the simpler XOR forms are not)
 //  * scales: 16 groups (4 chunks) of each of the 512 rows, two buffers that
 //    alternate every 4 chunks;
 //  * the words are dequantised to bf16 (u - 8) * s and fed to
 //    v_mfma_f32_16x16x32_bf16: MFMA step j of a chunk takes word j of every
 //    lane, so its 32-long reduction covers one 8-input slice of each of the
-//    four groups; the matching activations are read at those offsets.
+//    four groups; the matching activations are read at those offsets. The
+//    next step's dequantisation (VALU) is interleaved with this step's MFMAs.
 // One barrier per chunk: the copies of chunk c + 1 are issued before chunk c is
 // computed and waited for after it. Barriers are raw s_barrier with explicit
 // waits (the fence of __syncthreads() would also wait for the copies just
@@ -45,6 +49,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 #ifndef MOE_PREFILL_MAX_SUBTILES
@@ -87,21 +92,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// The eight codes of one word -> eight bf16 weights (u - 8) * s in input order:
-// even fields masked into the four bytes of one register, odd fields into
-// another, one v_cvt_f32_ubyte per code, fma(u, s, -8 s) exact in fp32, one
-// rounding to bf16. `mask` (0x0F0F0F0F) is a run-time value so that the
-// compiler keeps the byte form.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, uint32_t mask, float s, float neg8s) {
-  const uint32_t ev = w & mask;
-  const uint32_t od = (w >> 4) & mask;
+// (a & m) | c in one v_bitop3_b32 (truth table 0xEA over (a, m, c)).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
+}
+
+// The eight codes of one word -> eight bf16 weights (u - 8) * s in input order.
+// Fields k and k + 4 are OR-ed into the fp16 pattern 0x6400, which is exactly
+// the fp16 value 1024 + u (one shift and one v_bitop3 per pair); one mixed
+// fp16/fp32 FMA per code, fma(1024 + u, s, -1032 s), gives (u - 8) * s exactly
+// in fp32 (the product has at most 19 significant bits and so has 1032 s), and
+// it is rounded once to bf16.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float c1032) {
+  f32x2 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const h16x2 h = __builtin_bit_cast(h16x2, and_or(w >> (4 * k), 0x000F000Fu, 0x64006400u));
+    v[k] = f32x2{fmaf((float)h[0], s, c1032), fmaf((float)h[1], s, c1032)};  // u_k, u_{k+4}
+  }
   u32x4 r;
-  r[0] = pack_bf16x2(fmaf((float)(ev & 0xFFu), s, neg8s), fmaf((float)(od & 0xFFu), s, neg8s));
-  r[1] = pack_bf16x2(fmaf((float)((ev >> 8) & 0xFFu), s, neg8s),
-                     fmaf((float)((od >> 8) & 0xFFu), s, neg8s));
-  r[2] = pack_bf16x2(fmaf((float)((ev >> 16) & 0xFFu), s, neg8s),
-                     fmaf((float)((od >> 16) & 0xFFu), s, neg8s));
-  r[3] = pack_bf16x2(fmaf((float)(ev >> 24), s, neg8s), fmaf((float)(od >> 24), s, neg8s));
+  r[0] = pack_bf16x2(v[0][0], v[1][0]);
+  r[1] = pack_bf16x2(v[2][0], v[3][0]);
+  r[2] = pack_bf16x2(v[0][1], v[1][1]);
+  r[3] = pack_bf16x2(v[2][1], v[3][1]);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -121,6 +134,11 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 template <int PHASE>
 constexpr int tile_cols() { return PHASE == kGateUp ? kBN / 2 : kBN; }
+
+// Permutations of 16-byte pieces in LDS: the four groups of weight row R, the
+// sixteen pieces of activation row r.
+__device__ __forceinline__ int wslot(int R) { return (R >> 1) & 3; }
+__device__ __forceinline__ int aslot(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Weight row of work-group row R = 64 wave + 16 sub-tile + r.
 template <int PHASE>
@@ -158,7 +176,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   for (int i = 0; i < kAPerWave; ++i) {
     const int t = kAPerWave * wave + i;
     const int row = 4 * t + (lane >> 4);
-    const int piece = (lane & 15) ^ (row & 7);
+    const int piece = (lane & 15) ^ aslot(row & 15);
     int64_t src = -1;
     if (t < kACopies && row < MS * 16) {
       if (PHASE == kGateUp) {
@@ -187,7 +205,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int R = 16 * (4 * wave + i) + (lane >> 2);
-    const int g = (lane & 3) ^ ((R >> 1) & 3);
+    const int g = (lane & 3) ^ wslot(R);
     woff[i] = (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 8) + 4 * g) * 4);
   }
   auto copy_w = [&](uint8_t* dst, int ch) {
@@ -218,7 +236,12 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 
   // ---- this lane's LDS read offsets -----------------------------------------
   // weights: row R = 64 wave + 16 s + lr, group lq (permuted slot)
-  const int wread = (wave * 64 + lr) * kWRowBytes + ((lq ^ ((lr >> 1) & 3)) * 16);
+  int wread[kNSub];
+#pragma unroll
+  for (int s = 0; s < kNSub; ++s) {
+    const int R = wave * 64 + 16 * s + lr;
+    wread[s] = R * kWRowBytes + (lq ^ wslot(R)) * 16;
+  }
   // scales: row R, group 4 (chunk % 4) + lq
   const int sread = (wave * 64 + lr) * kSRowBytes + lq * 2;
   // activations: row 16 mi + lr, piece 4 lq + j (permuted slot)
@@ -230,27 +253,38 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* abuf, const uint8_t* wbuf, const float (&sc)[kNSub]) {
-    u32x4 w[kNSub];
+  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const float (&sc)[kNSub]) {
+    float c1032[kNSub];
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s)
-      w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread + s * 16 * kWRowBytes);
+    for (int s = 0; s < kNSub; ++s) c1032[s] = -1032.0f * sc[s];
+    bf16x8 bw[2][kNSub];  // this step's and the next step's weights
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) bw[0][s] = dequant8(w[s][0], sc[s], c1032[s]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 bw[kNSub];
+      bf16x8 a[MS];
+      const int apiece = ((4 * lq + j) ^ aslot(lr)) * 16;  // inputs 32 lq + 8 j
 #pragma unroll
-      for (int s = 0; s < kNSub; ++s)
-        bw[s] = dequant8(w[s][j], p.nibble_mask, sc[s], -8.0f * sc[s]);
-      const int apiece = ((4 * lq + j) ^ (lr & 7)) * 16;  // inputs 32 lq + 8 j
-#pragma unroll
-      for (int mi = 0; mi < MS; ++mi) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apiece);
+      for (int mi = 0; mi < MS; ++mi)
+        a[mi] = *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apiece);
+      if (j < 3) {
 #pragma unroll
         for (int s = 0; s < kNSub; ++s)
-          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[s], acc[mi][s], 0, 0, 0);
+          bw[(j + 1) & 1][s] = dequant8(w[s][j + 1], sc[s], c1032[s]);
       }
-      // one step's operands live at a time
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s)
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], bw[j & 1][s], acc[mi][s], 0, 0, 0);
+      // interleave: the activation reads first, then one MFMA per three VALU
+      // instructions of the next step's dequantisation
+      __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
+#pragma unroll
+      for (int i = 0; i < MS * kNSub; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -262,48 +296,46 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       sc[s] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sb + sread + s * 16 * kSRowBytes + g));
   };
 
+  // The chunk's scales and this wave's weight words are read from LDS first;
+  // the weight buffer is then free (each wave copies and reads only its own
+  // rows), so the copy of chunk ch + 2 goes into it at once: weights are
+  // fetched two chunks ahead, activations (shared by all waves, buffer freed
+  // by the barrier) one chunk ahead.
+  auto chunk = [&](int ch, uint8_t* abuf, uint8_t* anext, uint8_t* wbuf) {
+    float sc[kNSub];
+    read_scales(sc, ch);
+    u32x4 w[kNSub];
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread[s]);
+    wait_lgkm0();
+    __builtin_amdgcn_sched_barrier(0);
+    copy_a(anext, ch + 1);
+    copy_w(wbuf, ch + 2);
+    const bool new_s = ch % kSPeriod == 0 && ch / kSPeriod + 1 < nper;
+    if (new_s) copy_s(((ch / kSPeriod + 1) & 1) ? lds_s1 : lds_s0, ch / kSPeriod + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(abuf, w, sc);
+    // activations and weights of chunk ch + 1 in LDS (the copies of chunk
+    // ch + 2's weights and of the next scales may stay in flight); this
+    // chunk's LDS reads done before its activation buffer is overwritten
+    if (new_s) wait_vm<6>();
+    else wait_vm<4>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+
   // ---- pipeline -----------------------------------------------------------
   copy_w(lds_w0, 0);
+  copy_w(lds_w1, 1);
   copy_a(lds_a0, 0);
   copy_s(lds_s0, 0);
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  // even chunk: buffers 0; its scales are read before the copies are issued
-  auto even_chunk = [&](int ch) {
-    float sc[kNSub];
-    read_scales(sc, ch);
-    __builtin_amdgcn_sched_barrier(0);
-    copy_w(lds_w1, ch + 1);
-    copy_a(lds_a1, ch + 1);
-    const bool new_s = ch % kSPeriod == 0 && ch / kSPeriod + 1 < nper;
-    if (new_s) copy_s(((ch / kSPeriod + 1) & 1) ? lds_s1 : lds_s0, ch / kSPeriod + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(lds_a0, lds_w0, sc);
-    // chunk ch + 1 in LDS (a scale copy may stay in flight); this chunk's LDS
-    // reads done before its buffers are overwritten
-    if (new_s) wait_vm<2>();
-    else wait_vm<0>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-  };
-  // odd chunk: buffers 1 (kSPeriod is even: no scale copy starts here)
-  auto odd_chunk = [&](int ch) {
-    float sc[kNSub];
-    read_scales(sc, ch);
-    __builtin_amdgcn_sched_barrier(0);
-    copy_w(lds_w0, ch + 1);
-    copy_a(lds_a0, ch + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(lds_a1, lds_w1, sc);
-    wait_vm<0>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-  };
   // whole pairs (the chunk count is even; a loop with a second exit between
   // the halves makes the register allocator move the accumulators)
   for (int ch = 0; ch < nch; ch += 2) {
-    even_chunk(ch);
-    odd_chunk(ch + 1);
+    chunk(ch, lds_a0, lds_a1, lds_w0);
+    chunk(ch + 1, lds_a1, lds_a0, lds_w1);
   }
 
   // ---- epilogue: lane holds rows 4 lq + i of each 16-row sub-tile, column lr
@@ -335,14 +367,23 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   }
 }
 
-// Work-groups: max_blocks x tiles, block-major (the default round-robin
-// placement spreads a block's tiles over the XCDs).
+// Work-groups: all column tiles of block b run on XCD b % 8. Work-groups are
+// dispatched round-robin over the 8 XCDs in id order, so the s-th work-group
+// that XCD x receives (id 8 s + x) takes tile s % n_tiles of block
+// 8 (s / n_tiles) + x: a block's activations are fetched into one XCD's L2 and
+// shared by its tiles there, and the blocks past the last bucket (which exit
+// at once) are spread evenly over the XCDs. The grid holds a multiple of 8
+// blocks.
+constexpr int kXcds = 8;
+
 template <int PHASE>
 __global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p) {
   const int n_tiles = p.N / tile_cols<PHASE>();
-  const int mblk = blockIdx.x / n_tiles;
-  const int tile = blockIdx.x - mblk * n_tiles;
-  if ((int64_t)mblk * kBM >= *p.n_padded) return;
+  const int x = blockIdx.x % kXcds;
+  const int sx = blockIdx.x / kXcds;
+  const int mblk = (sx / n_tiles) * kXcds + x;
+  const int tile = sx - (sx / n_tiles) * n_tiles;
+  if (mblk >= p.max_blocks || (int64_t)mblk * kBM >= *p.n_padded) return;
   // bucket rows of the block (padding sits at its end), in 16-row sub-tiles
   const int64_t row0 = (int64_t)mblk * kBM;
   const int lane = threadIdx.x & 63;
@@ -366,7 +407,8 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
   const int64_t arows = PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM;
   const int64_t nw = PHASE == kGateUp ? 2 * (int64_t)p.I : p.N;
   if (arows * p.K * 2 > 0x7fffffff || nw * p.K / 2 > 0x7fffffff) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)p.max_blocks * (p.N / tile_cols<PHASE>());
+  const int64_t blocks = ((int64_t)p.max_blocks + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = blocks * (p.N / tile_cols<PHASE>());
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
