@@ -36,8 +36,11 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s vs roofline"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+# block_m of the paths whose gate_up launch also carries the shared expert
+# (small-batch and tiled kernels); prefill-sized blocks give it its own launch
+SINGLE_LAUNCH_BLOCK_M = (4, 16, 64)
 GEMM_SRCS = [os.path.join(ROOT, "w4a16_int4_grouped_moe_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_small.hip")]
+             for f in ("gemm.hip", "gemm_small.hip", "gemm_prefill.hip")]
 
 
 # ----------------------------------------------------------------------------
@@ -51,7 +54,10 @@ def w2_bytes(H, I):
     return H * I // 2 + H * (I // 32) * 2
 
 
-def work(T, H, I, k, ids, n_local, base, shared):
+def work(T, H, I, k, ids, n_local, base, shared, shared_in_kernel=True):
+    """Bytes the layer must move and FLOPs it must do; gate_up_* are those of the
+    launch that carries the routed experts' gate_up (it also carries the shared
+    expert unless that runs in a launch of its own: shared_in_kernel False)."""
     import numpy as np
 
     flat = np.asarray(ids).ravel()
@@ -61,10 +67,11 @@ def work(T, H, I, k, ids, n_local, base, shared):
     s13 = 2 * I * H * 2 if shared else 0
     s2 = H * I * 2 if shared else 0
     ts = T if shared else 0
-    gate_up_bytes = U * w13_bytes(H, I) + s13 + T * H * 2 + (P + ts) * I * 2
     layer_bytes = U * (w13_bytes(H, I) + w2_bytes(H, I)) + s13 + s2 + 2 * T * H * 2 + T * k * 8
-    gate_up_flops = (P + ts) * 2 * (2 * I) * H
     layer_flops = (P + ts) * (2 * (2 * I) * H + 2 * H * I)
+    ks = ts if shared_in_kernel else 0
+    gate_up_bytes = U * w13_bytes(H, I) + (s13 if ks else 0) + T * H * 2 + (P + ks) * I * 2
+    gate_up_flops = (P + ks) * 2 * (2 * I) * H
     return dict(P=P, U=U, gate_up_bytes=gate_up_bytes, layer_bytes=layer_bytes,
                 gate_up_flops=gate_up_flops, layer_flops=layer_flops)
 
@@ -110,23 +117,37 @@ def traffic_record(workload):
     return None
 
 
-def cpu_baseline(w, x, ids, wts, shared, n_tokens):
+def cpu_baseline(calls, shared, n_tokens, seconds):
+    """The fp64 oracle on a bounded sample of the same workload: the first
+    n_tokens tokens of each batch, batch after batch, until `seconds` of wall
+    time have passed (at least one pass over every batch)."""
     import numpy as np
 
     import moe_inputs as mi
     import oracle
 
-    rows = np.arange(min(n_tokens, w.T))
-    used, remap = mi.compact_routing(ids, rows, w.expert_base, w.n_local)
-    bank = mi.weight_bank(w.seed_bank, w.geo.hidden, w.geo.inter, used or [0])
     threads = oracle.oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.forward(x[rows], remap, wts[rows], bank.packed_w13, bank.scales_w13,
-                   bank.packed_w2, bank.scales_w2, shared, 0, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"first {len(rows)} tokens of the {w.name} T={w.T} batch, fp64 C oracle, "
+    jobs = []
+    for c in calls:
+        w = c["w"]
+        rows = np.arange(min(n_tokens, w.T))
+        used, remap = mi.compact_routing(c["ids_np"], rows, w.expert_base, w.n_local)
+        bank = mi.weight_bank(w.seed_bank, w.geo.hidden, w.geo.inter, used or [0])
+        jobs.append((c["x_np"][rows], remap, c["wts_np"][rows], bank))
+    done, n_calls, t0 = 0, 0, time.perf_counter()
+    while True:
+        for x, remap, wts, bank in jobs:
+            oracle.forward(x, remap, wts, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                           bank.scales_w2, shared, 0, threads=threads)
+            done += x.shape[0]
+            n_calls += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    w = calls[0]["w"]
+    return {"value": round(done / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} tokens: {n_calls} oracle calls on the first <= {n_tokens} tokens of "
+                      f"each {w.name} batch ({[c['T'] for c in calls]}), fp64 C oracle, "
                       f"{dt:.1f} s wall on {threads} threads"}
 
 
@@ -138,7 +159,9 @@ def main():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "ep", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=32,
-                    help="tokens of the CPU-oracle sample (0 disables it)")
+                    help="tokens per batch of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time of the CPU-oracle sample (repeated passes)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -175,14 +198,16 @@ def main():
         b = bank if i == 0 else {k: v.clone() for k, v in bank.items()}
         s = shared if (i == 0 or shared is None) else shared.clone()
         p = moe.problem(T, g.hidden, g.inter, w.n_local, g.top_k, w.expert_base)
+        bm = moe.forward_block_m(p)
         calls.append(dict(
             w=w, T=T, x_np=x, ids_np=ids, wts_np=wts,
             args=(mi.to_device(x, dev), mi.to_device(ids, dev), mi.to_device(wts, dev),
                   b["packed_w13"], b["scales_w13"], b["packed_w2"], b["scales_w2"], s),
             out=torch.empty((T, g.hidden), dtype=torch.bfloat16, device=dev),
             ws=torch.empty(max(moe.workspace_size(p), 1), dtype=torch.uint8, device=dev),
-            work=work(T, g.hidden, g.inter, g.top_k, ids, w.n_local, w.expert_base, g.shared),
-            base=w.expert_base))
+            work=work(T, g.hidden, g.inter, g.top_k, ids, w.n_local, w.expert_base, g.shared,
+                      shared_in_kernel=bm in SINGLE_LAUNCH_BLOCK_M),
+            bm=bm, base=w.expert_base))
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     print(f"[bench] setup {t_setup:.1f} s; workload {args.workload} batches {batches}",
@@ -197,9 +222,10 @@ def main():
             run(c)
     torch.cuda.synchronize()
 
-    # timed region: only the two events that bracket the dominant kernel
-    # (gate_up) are recorded, so that event packets add little to the step time
-    events = [[[None, hip.event(), hip.event(), None, None] for _ in calls]
+    # timed region: only the two events that bracket the dominant kernel (the
+    # routed experts' gate_up launch) are recorded, so that event packets add
+    # little to the step time
+    events = [[[None, hip.event(), None, None, None, hip.event(), None] for _ in calls]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -215,7 +241,7 @@ def main():
     # after the timed region: a short pass with all stage events, for the
     # per-stage breakdown (these extra event packets lengthen the calls a little)
     n_diag = min(5, args.steps)
-    diag = [[[hip.event() for _ in range(5)] for _ in calls] for _ in range(n_diag)]
+    diag = [[[hip.event() for _ in range(7)] for _ in calls] for _ in range(n_diag)]
     for step in range(n_diag):
         for c, ev in zip(calls, diag[step]):
             run(c, ev)
@@ -225,7 +251,7 @@ def main():
     per_batch = []
     gate_up_ms, gate_up_bytes, gate_up_flops = [], [], []
     for ci, c in enumerate(calls):
-        gu = np.array([hip.elapsed_ms(events[s][ci][1], events[s][ci][2])
+        gu = np.array([hip.elapsed_ms(events[s][ci][1], events[s][ci][5])
                        for s in range(args.steps)])
         st = np.array([[hip.elapsed_ms(diag[s][ci][j], diag[s][ci][j + 1]) for j in range(4)]
                        for s in range(n_diag)])
@@ -239,6 +265,10 @@ def main():
             layer_tflops=round(wk["layer_flops"] / (float(np.median(call_ms)) / 1e3) / 1e12, 2),
             experts_hit=wk["U"], pairs=wk["P"],
             gate_up_us=round(float(gu.mean()) * 1e3, 2),
+            routed_us={"gate_up": round(float(np.mean([hip.elapsed_ms(diag[s][ci][1], diag[s][ci][5])
+                                                       for s in range(n_diag)])) * 1e3, 2),
+                       "down": round(float(np.mean([hip.elapsed_ms(diag[s][ci][2], diag[s][ci][6])
+                                                    for s in range(n_diag)])) * 1e3, 2)},
             stage_us={n: round(float(v) * 1e3, 2) for n, v in zip(stage_names, avg)}))
         gate_up_ms.append(float(gu.mean()))
         gate_up_bytes.append(wk["gate_up_bytes"])
@@ -261,9 +291,15 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
     bms = [moe.forward_block_m(moe.problem(T, g.hidden, g.inter, w0.n_local, g.top_k))
            for T in batches]
-    roof["kernel"] = ("small_gemm_kernel<gate_up> (int4 dequant + MFMA 4x4x4, fused SwiGLU)"
-                      if all(b == 4 for b in bms) else
-                      "grouped_gemm_kernel<gate_up> (int4 dequant + MFMA 16x16x32, fused SwiGLU)")
+    if all(b == 4 for b in bms):
+        roof["kernel"] = ("small_gemm_kernel<gate_up>: routed + shared experts, int4 dequant + "
+                          "MFMA 4x4x4, fused SwiGLU")
+    elif all(b in SINGLE_LAUNCH_BLOCK_M for b in bms):
+        roof["kernel"] = ("grouped_gemm_kernel<gate_up>: routed + shared experts, int4 dequant + "
+                          "MFMA 16x16x32, fused SwiGLU")
+    else:
+        roof["kernel"] = ("prefill_gemm_kernel<gate_up>: routed experts, int4 dequant + "
+                          "MFMA 16x16x32, fused SwiGLU")
     roof["algorithmic_per_launch"] = (float(np.mean(gate_up_flops)) if roof["bound"] == "mfma"
                                       else float(np.mean(gate_up_bytes)))
     roof["avg_launch_us"] = round(mean_s * 1e6, 2)
@@ -277,9 +313,7 @@ def main():
 
     cpu = None
     if args.cpu_tokens > 0:
-        c = calls[-1]
-        cpu = cpu_baseline(c["w"], c["x_np"], c["ids_np"], c["wts_np"], shared_np,
-                           args.cpu_tokens)
+        cpu = cpu_baseline(calls, shared_np, args.cpu_tokens, args.cpu_seconds)
 
     if args.workload == "decode":
         wl = ("Kimi-K2.6-shape W4A16 MoE layer decode: hidden 7168, moe_intermediate 2048, "

@@ -137,9 +137,13 @@ int moe_w4a16_forward(const void *x, const int32_t *topk_ids, const float *topk_
 /*
  * moe_w4a16_forward with stage timing: identical work and results, and in
  * addition records the caller's HIP events (hipEvent_t, created by the caller;
- * NULL entries are skipped) on `stream`: stage_events[0] before the bucketing,
- * [1] before the gate_up GEMM, [2] before the down GEMM, [3] before the
- * combine and [4] after it. Used to time each kernel on its own stream.
+ * stage_events holds 7 entries, NULL entries are skipped) on `stream`:
+ * [0] before the bucketing, [1] before the gate_up GEMM, [2] before the down
+ * GEMM, [3] before the combine, [4] after it, [5] after the routed experts'
+ * gate_up launch and [6] after the routed experts' down launch. Where the
+ * shared expert runs in a launch of its own (prefill-sized blocks) it follows
+ * [5] / [6]; elsewhere [5] / [6] directly follow the phase's single launch.
+ * Used to time each kernel on its own stream.
  */
 int moe_w4a16_forward_timed(const void *x, const int32_t *topk_ids, const float *topk_weights,
                             const int32_t *packed_w13, const void *scales_w13,

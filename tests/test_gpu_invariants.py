@@ -118,3 +118,32 @@ def test_graph_capture_replay(setup):
         # unrelated eager work between replays
         moe.forward(xs[:7], ids_d[:7], w_d[:7], *args[3:])
         torch.cuda.synchronize()
+
+
+def test_timed_entry_point(setup):
+    """moe_w4a16_forward_timed: the same output as the plain call, and its seven
+    events recorded in stream order."""
+    import ctypes
+    import torch
+
+    dev, bank, bank_dev, x, ids, w, sw = setup
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    ev = []
+    for _ in range(7):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        ev.append(e.value)
+    import w4a16_int4_grouped_moe_amd as moe
+
+    d = lambda a: mi.to_device(a, dev)
+    plain = bits(run_layer(dev, x, ids, w, bank_dev, sw))
+    out = moe.forward(d(x), d(ids), d(w), bank_dev["packed_w13"], bank_dev["scales_w13"],
+                      bank_dev["packed_w2"], bank_dev["scales_w2"], d(sw), stage_events=ev)
+    assert np.array_equal(bits(out), plain)
+    ms = ctypes.c_float()
+    for a, b in [(0, 1), (1, 5), (5, 2), (2, 6), (6, 3), (3, 4)]:
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[a], ev[b]) == 0
+        assert ms.value >= 0.0

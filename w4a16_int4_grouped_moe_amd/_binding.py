@@ -139,7 +139,7 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
     packed_w13 int32 [E, 2I, H/8]; scales_w13 bf16 [E, 2I, H/32];
     packed_w2 int32 [E, H, I/8]; scales_w2 bf16 [E, H, I/32];
     shared_w bf16 [2I*H + H*I] or None. Returns out bf16 [T, H].
-    stage_events: optional sequence of 5 raw hipEvent_t handles (int or None)
+    stage_events: optional sequence of 7 raw hipEvent_t handles (int or None)
     recorded between the stages (see moe_w4a16_forward_timed).
     """
     torch = _torch()
@@ -191,9 +191,9 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
     if stage_events is None:
         st = library().moe_w4a16_forward(*args)
     else:
-        if len(stage_events) != 5:
-            raise ValueError("stage_events needs 5 entries")
-        ev = (ctypes.c_void_p * 5)(*[e or None for e in stage_events])
+        if len(stage_events) != 7:
+            raise ValueError("stage_events needs 7 entries")
+        ev = (ctypes.c_void_p * 7)(*[e or None for e in stage_events])
         st = library().moe_w4a16_forward_timed(*args, ev)
     _check(st)
     return out

@@ -163,7 +163,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   const int32_t H = p->hidden, I = p->inter, E = p->num_experts, k = p->top_k;
   const uint16_t* sw = static_cast<const uint16_t*>(shared_w);
 
-  auto mark = [&](int i) -> hipError_t {
+  auto mark = [&](int i) -> hipError_t {  // stage_events[i], if given
     if (events && events[i]) return hipEventRecord((hipEvent_t)events[i], strm);
     return hipSuccess;
   };
@@ -175,13 +175,20 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
 
   // One GEMM phase. Prefill blocks: the routed experts in the prefill kernel,
   // the shared expert in a second launch of the tiled kernel (64-token tiles).
-  auto gemm = [&](const moe::GemmParams& gp, bool gate_up) -> hipError_t {
-    if (L.bm == 4)
-      return gate_up ? moe::launch_gate_up_small(gp, strm) : moe::launch_down_small(gp, strm);
-    if (L.bm != moe::prefill_block_m())
-      return gate_up ? moe::launch_gate_up(gp, L.bm, strm) : moe::launch_down(gp, L.bm, strm);
-    hipError_t e = gate_up ? moe::launch_gate_up_prefill(gp, strm)
-                           : moe::launch_down_prefill(gp, strm);
+  // Event `after_routed` is recorded once the routed experts' launch is
+  // queued (on the single-launch paths it follows the whole phase).
+  auto gemm = [&](const moe::GemmParams& gp, bool gate_up, int after_routed) -> hipError_t {
+    hipError_t e;
+    if (L.bm == 4) {
+      e = gate_up ? moe::launch_gate_up_small(gp, strm) : moe::launch_down_small(gp, strm);
+      return e != hipSuccess ? e : mark(after_routed);
+    }
+    if (L.bm != moe::prefill_block_m()) {
+      e = gate_up ? moe::launch_gate_up(gp, L.bm, strm) : moe::launch_down(gp, L.bm, strm);
+      return e != hipSuccess ? e : mark(after_routed);
+    }
+    e = gate_up ? moe::launch_gate_up_prefill(gp, strm) : moe::launch_down_prefill(gp, strm);
+    if (e == hipSuccess) e = mark(after_routed);
     if (e != hipSuccess || !gp.wshared) return e;
     moe::GemmParams gs = gp;
     gs.max_blocks = 0;  // shared-expert tiles only
@@ -210,7 +217,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.K = H;
   g.N = I;
   if ((err = mark(1)) != hipSuccess) return hip_status(err);
-  err = gemm(g, true);
+  err = gemm(g, true, 5);
   if (err != hipSuccess) return hip_status(err);
 
   // down
@@ -224,7 +231,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.K = I;
   g.N = H;
   if ((err = mark(2)) != hipSuccess) return hip_status(err);
-  err = gemm(g, false);
+  err = gemm(g, false, 6);
   if (err != hipSuccess) return hip_status(err);
 
   if ((err = mark(3)) != hipSuccess) return hip_status(err);
