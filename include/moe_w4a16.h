@@ -102,12 +102,26 @@ int moe_w4a16_align_capacity(const moe_w4a16_problem *p, int32_t block_m,
  *                block of block_m entries of sorted_ids.
  *   n_padded     int32 [1] (device, out): number of meaningful sorted_ids.
  *
+ *   scratch      device, scratch_bytes long, or NULL. NULL: the bucketing runs
+ *                in one work-group (one launch; suits small T*k). Otherwise at
+ *                least moe_w4a16_align_scratch_size bytes: it runs in many
+ *                work-groups (three launches, per-chunk counts in scratch).
+ *                Both give identical output.
+ *
  * 1 <= block_m <= 1024. Returns MOE_ERR_WORKSPACE if a capacity is below the
- * value moe_w4a16_align_capacity reports.
+ * value moe_w4a16_align_capacity reports, or if scratch is given and shorter
+ * than moe_w4a16_align_scratch_size.
  */
 int moe_w4a16_align(const int32_t *topk_ids, const moe_w4a16_problem *p, int32_t block_m,
                     int32_t *sorted_ids, int64_t sorted_capacity, int32_t *block_expert,
-                    int64_t block_capacity, int32_t *n_padded, void *stream);
+                    int64_t block_capacity, int32_t *n_padded, void *scratch,
+                    size_t scratch_bytes, void *stream);
+
+/*
+ * Scratch bytes (host out) of the many-work-group bucketing for this problem:
+ * one int32 per (chunk of 256 pairs, local expert).
+ */
+int moe_w4a16_align_scratch_size(const moe_w4a16_problem *p, size_t *bytes);
 
 /*
  * The layer.

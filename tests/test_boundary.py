@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
-        "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_forward",
+        "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_align_scratch_size",
+        "moe_w4a16_forward",
         "moe_w4a16_forward_block_m", "moe_w4a16_forward_timed", "moe_w4a16_status_string",
         "moe_w4a16_workspace_size"])
 
@@ -137,10 +138,10 @@ def test_align_argument_errors(lib):
     f = ctypes.c_void_p
     ok = dict(ids=f(0x10000), sorted=f(0x20000), blocks=f(0x30000), npad=f(0x40000))
 
-    def call(bm=16, cs=cap_s, cb=cap_b, **over):
+    def call(bm=16, cs=cap_s, cb=cap_b, scratch=None, nbytes=0, **over):
         a = dict(ok, **over)
         return lib.moe_w4a16_align(a["ids"], ctypes.byref(p), bm, a["sorted"], cs, a["blocks"],
-                                   cb, a["npad"], None)
+                                   cb, a["npad"], scratch, nbytes, None)
 
     assert call(bm=0) == moe.MOE_ERR_SHAPE
     assert call(bm=2048) == moe.MOE_ERR_SHAPE
@@ -149,6 +150,10 @@ def test_align_argument_errors(lib):
     assert call(ids=None) == moe.MOE_ERR_NULL
     assert call(npad=None) == moe.MOE_ERR_NULL
     assert call(sorted=f(0x20004)) == moe.MOE_ERR_ALIGNMENT
+    need = moe.align_scratch_size(p)
+    assert need == 4 * ((p.num_tokens * p.top_k + 255) // 256) * p.num_experts
+    assert call(scratch=f(0x50000), nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(scratch=f(0x50008), nbytes=need) == moe.MOE_ERR_ALIGNMENT
     with pytest.raises(ValueError):
         moe.align_capacity(p, 0)
 

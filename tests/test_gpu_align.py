@@ -1,4 +1,5 @@
-"""Bucketing on the GPU equals the oracle's stable sort, bit for bit."""
+"""Bucketing on the GPU equals the oracle's stable sort, bit for bit, in both
+forms: one work-group, and many work-groups with per-chunk counts."""
 import numpy as np
 import pytest
 
@@ -16,12 +17,13 @@ def dev():
     return torch.device("cuda:0")
 
 
-def gpu_align(dev, ids, E, base, bm):
+def gpu_align(dev, ids, E, base, bm, many_groups=False):
     import torch
 
     import w4a16_int4_grouped_moe_amd as moe
 
-    s, b, n = moe.align(mi.to_device(ids, dev), E, bm, expert_base=base)
+    s, b, n = moe.align(mi.to_device(ids, dev), E, bm, expert_base=base,
+                        many_groups=many_groups)
     torch.cuda.synchronize()
     n = int(n.cpu()[0])
     return s.cpu().numpy()[:n], b.cpu().numpy()[:n // bm], n
@@ -30,11 +32,12 @@ def gpu_align(dev, ids, E, base, bm):
 def compare(dev, ids, E, base, bm, label):
     print(f"[align] {label} T={ids.shape[0]} k={ids.shape[1]} E={E} base={base} bm={bm}",
           flush=True)
-    s, b, n = gpu_align(dev, ids, E, base, bm)
     rs, rb, rn = oracle.align(ids, E, base, bm)
-    assert n == rn, (n, rn)
-    assert np.array_equal(s, rs), label
-    assert np.array_equal(b, rb), label
+    for many in (False, True):
+        s, b, n = gpu_align(dev, ids, E, base, bm, many)
+        assert n == rn, (label, many, n, rn)
+        assert np.array_equal(s, rs), (label, many)
+        assert np.array_equal(b, rb), (label, many)
 
 
 WORKLOADS = [("tiny", None), ("decode", 1), ("decode", 8), ("decode", 32), ("decode", 64),
@@ -42,7 +45,7 @@ WORKLOADS = [("tiny", None), ("decode", 1), ("decode", 8), ("decode", 32), ("dec
 
 
 @pytest.mark.parametrize("name,T", WORKLOADS)
-@pytest.mark.parametrize("bm", [1, 4, 16, 64, 128])
+@pytest.mark.parametrize("bm", [1, 4, 16, 64, 96, 128])
 def test_align_workloads(dev, name, T, bm):
     w = mi.workload(name, T)
     ids, _ = mi.make_routing(w)
@@ -72,8 +75,9 @@ def test_align_edge_cases(dev):
 def test_align_deterministic(dev):
     w = mi.workload("skew", 512)
     ids, _ = mi.make_routing(w)
-    first = gpu_align(dev, ids, 384, 0, 16)
-    for _ in range(20):
-        again = gpu_align(dev, ids, 384, 0, 16)
-        assert again[2] == first[2]
-        assert np.array_equal(again[0], first[0]) and np.array_equal(again[1], first[1])
+    for many in (False, True):
+        first = gpu_align(dev, ids, 384, 0, 16, many)
+        for _ in range(10):
+            again = gpu_align(dev, ids, 384, 0, 16, many)
+            assert again[2] == first[2]
+            assert np.array_equal(again[0], first[0]) and np.array_equal(again[1], first[1])

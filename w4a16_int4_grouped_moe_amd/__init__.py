@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     Problem,
     align,
     align_capacity,
+    align_scratch_size,
     forward,
     forward_block_m,
     library,

@@ -57,13 +57,14 @@ def library():
                                                  ctypes.POINTER(ctypes.c_int64),
                                                  ctypes.POINTER(ctypes.c_int64)]
         lib.moe_w4a16_align.argtypes = [P, PP, ctypes.c_int32, P, ctypes.c_int64, P,
-                                        ctypes.c_int64, P, P]
+                                        ctypes.c_int64, P, P, ctypes.c_size_t, P]
+        lib.moe_w4a16_align_scratch_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_w4a16_forward.argtypes = [P] * 9 + [PP, P, ctypes.c_size_t, P]
         lib.moe_w4a16_forward_timed.argtypes = [P] * 9 + [PP, P, ctypes.c_size_t, P, P]
         lib.moe_w4a16_status_string.argtypes = [ctypes.c_int]
         lib.moe_w4a16_status_string.restype = ctypes.c_char_p
-        for f in ("workspace_size", "forward_block_m", "align_capacity", "align", "forward",
-                  "forward_timed"):
+        for f in ("workspace_size", "forward_block_m", "align_capacity", "align",
+                  "align_scratch_size", "forward", "forward_timed"):
             getattr(lib, "moe_w4a16_" + f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -199,10 +200,18 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
     return out
 
 
-def align(topk_ids, num_experts: int, block_m: int, expert_base: int = 0):
+def align_scratch_size(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().moe_w4a16_align_scratch_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def align(topk_ids, num_experts: int, block_m: int, expert_base: int = 0,
+          many_groups: bool = False):
     """Token/expert bucketing: returns (sorted_ids, block_expert, n_padded)
     int32 device tensors sized to the capacities; only the first n_padded
-    sorted_ids and n_padded/block_m block_expert entries are meaningful."""
+    sorted_ids and n_padded/block_m block_expert entries are meaningful.
+    many_groups: use the many-work-group form (with its scratch)."""
     torch = _torch()
     dev = topk_ids.device
     _need(topk_ids, "topk_ids", torch.int32, 2, dev)
@@ -212,8 +221,13 @@ def align(topk_ids, num_experts: int, block_m: int, expert_base: int = 0):
     sorted_ids = torch.empty(max(cap_s, 4), dtype=torch.int32, device=dev)
     block_expert = torch.empty(max(cap_b, 4), dtype=torch.int32, device=dev)
     n_padded = torch.empty(4, dtype=torch.int32, device=dev)
+    scratch, nbytes = None, 0
+    if many_groups:
+        nbytes = align_scratch_size(p)
+        scratch = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     st = library().moe_w4a16_align(
         topk_ids.data_ptr(), ctypes.byref(p), block_m, sorted_ids.data_ptr(), cap_s,
-        block_expert.data_ptr(), cap_b, n_padded.data_ptr(), _stream_handle(dev))
+        block_expert.data_ptr(), cap_b, n_padded.data_ptr(),
+        None if scratch is None else scratch.data_ptr(), nbytes, _stream_handle(dev))
     _check(st)
     return sorted_ids, block_expert, n_padded[:1]

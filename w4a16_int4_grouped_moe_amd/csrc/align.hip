@@ -7,7 +7,7 @@
 // (Changes list) need such a bucketing; the pages leave its form open, and this
 // ordering (ascending p inside a bucket) is the one the library fixes.
 //
-// One work-group of 16 waves does everything in a single launch:
+// Small P: one work-group of 16 waves does everything in a single launch:
 //   1. each wave histograms a contiguous chunk of pairs (LDS atomics; counts
 //      do not depend on order);
 //   2. per expert: prefix of the wave counts, padded size, block-wide scan of
@@ -129,7 +129,155 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   }
 }
 
+// ---- many work-groups (large P): count, scan, scatter ----------------------
+// The pairs are cut into chunks of kChunk consecutive pairs, one per wave.
+// count: each wave histograms its chunk into counts[chunk][E] (plain stores).
+// scan:  one work-group turns the counts into each chunk's first position per
+//        expert (bucket offset + pairs of that expert in earlier chunks), and
+//        writes n_padded, the padding and the block map.
+// scatter: each wave places its chunk's pairs exactly as the single-group
+//        kernel does (ranks from ballots), from its own cursors.
+// The result is identical to the single-group kernel's.
+constexpr int kMultiThreads = 256;
+constexpr int kMultiWaves = kMultiThreads / 64;
+constexpr int kChunk = 256;  // pairs per wave
+
+__global__ __launch_bounds__(kMultiThreads) void align_count_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int E, int base, int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];  // [kMultiWaves][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kMultiWaves * E; i += kMultiThreads) hist[i] = 0;
+  __syncthreads();
+  const int64_t q = (int64_t)blockIdx.x * kMultiWaves + wave;  // chunk
+  const int64_t c0 = q * kChunk;
+  const int64_t c1 = c0 + kChunk < P ? c0 + kChunk : P;
+  for (int64_t p = c0 + lane; p < c1; p += 64) {
+    const int e = ids[p] - base;
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave * E + e], 1);
+  }
+  __syncthreads();
+  const int64_t nq = (P + kChunk - 1) / kChunk;
+  for (int i = tid; i < kMultiWaves * E; i += kMultiThreads) {
+    const int64_t qq = (int64_t)blockIdx.x * kMultiWaves + i / E;
+    if (qq < nq) counts[qq * E + i % E] = hist[i];
+  }
+}
+
+__global__ __launch_bounds__(1024) void align_scan_kernel(
+    int64_t P, int E, int bm, int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ n_padded_out) {
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nq = (P + kChunk - 1) / kChunk;
+  // per expert: exclusive prefix over the chunks (in place), total; sixteen
+  // independent loads at a time
+  int run = 0;
+  if (tid < E) {
+    for (int64_t q0 = 0; q0 < nq; q0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = q0 + u < nq ? counts[(q0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (q0 + u < nq) counts[(q0 + u) * E + tid] = run;
+        run += c[u];
+      }
+    }
+  }
+  const int pad = tid < E ? (run + bm - 1) / bm * bm : 0;
+  int incl = pad;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int u = __shfl_up(s, d);
+      if (lane >= d) s += u;
+    }
+    if (lane < 16) wsum[lane] = s;
+  }
+  __syncthreads();
+  const int off = incl - pad + (wave > 0 ? wsum[wave - 1] : 0);
+  if (tid == 1023) *n_padded_out = off + pad;
+  if (tid < E) {
+    for (int64_t q = 0; q < nq; ++q) counts[q * E + tid] += off;
+    for (int r = run; r < pad; ++r) sorted_ids[off + r] = (int32_t)P;
+    for (int b = off / bm; b < (off + pad) / bm; ++b) block_expert[b] = tid;
+  }
+}
+
+__global__ __launch_bounds__(kMultiThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int E, int base,
+    const int32_t* __restrict__ cursors, int32_t* __restrict__ sorted_ids) {
+  extern __shared__ int32_t cur_lds[];  // [kMultiWaves][E]
+  volatile int32_t* cur = cur_lds;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nq = (P + kChunk - 1) / kChunk;
+  for (int i = tid; i < kMultiWaves * E; i += kMultiThreads) {
+    const int64_t qq = (int64_t)blockIdx.x * kMultiWaves + i / E;
+    cur[i] = qq < nq ? cursors[qq * E + i % E] : 0;
+  }
+  __syncthreads();
+  const int64_t q = (int64_t)blockIdx.x * kMultiWaves + wave;
+  const int64_t c0 = q * kChunk;
+  const int64_t c1 = c0 + kChunk < P ? c0 + kChunk : P;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t p0 = c0; p0 < c1; p0 += 64) {
+    const int64_t p = p0 + lane;
+    int e = -1;
+    if (p < c1) {
+      const int t = ids[p] - base;
+      if ((unsigned)t < (unsigned)E) e = t;
+    }
+    uint64_t active = __ballot(e >= 0);
+    int rank = 0, group = 0;
+    while (active) {
+      const int leader = __builtin_ctzll(active);
+      const int key = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(e == key);
+      if (e == key) {
+        rank = __popcll(m & lt_mask);
+        group = __popcll(m);
+      }
+      active &= ~m;
+    }
+    if (e >= 0) {
+      const int cursor = cur[wave * E + e];
+      sorted_ids[cursor + rank] = (int32_t)p;
+      if (rank == 0) cur[wave * E + e] = cursor + group;
+    }
+  }
+}
+
 }  // namespace
+
+int64_t align_scratch_ints(int64_t P, int32_t E) {
+  return (P + kChunk - 1) / kChunk * E;
+}
+
+hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
+                              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                              int32_t* n_padded, int32_t* scratch, hipStream_t stream) {
+  if (P == 0) return launch_align(topk_ids, P, E, base, block_m, sorted_ids, block_expert,
+                                  n_padded, stream);
+  const int64_t nq = (P + kChunk - 1) / kChunk;
+  const int64_t groups = (nq + kMultiWaves - 1) / kMultiWaves;
+  if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const size_t lds = sizeof(int32_t) * (size_t)kMultiWaves * E;
+  hipLaunchKernelGGL(align_count_kernel, dim3((unsigned)groups), dim3(kMultiThreads), lds,
+                     stream, topk_ids, P, E, base, scratch);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, stream, P, E, block_m, scratch,
+                     sorted_ids, block_expert, n_padded);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)groups), dim3(kMultiThreads), lds,
+                     stream, topk_ids, P, E, base, scratch, sorted_ids);
+  return hipGetLastError();
+}
 
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,

@@ -50,8 +50,11 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
   return P >= 32 * E ? 64 : 16;
 }
 
+// Bucketing in many work-groups (three launches) from this many pairs on.
+constexpr int64_t kAlignMultiMin = 8192;
+
 struct Layout {
-  size_t sorted_ids, block_expert, meta, h, y, hs, s, total;
+  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, total;
   int64_t cap_rows;
   int32_t max_blocks, bm;
 };
@@ -71,6 +74,9 @@ Layout layout(const moe_w4a16_problem* p) {
   L.y = o; o = round_up(o + 4 * P * H);
   L.hs = o; o = round_up(o + 2 * T * I);
   L.s = o; o = round_up(o + 4 * T * H);
+  L.align_scratch = o;
+  if ((int64_t)P >= kAlignMultiMin)
+    o = round_up(o + 4 * (size_t)moe::align_scratch_ints((int64_t)P, p->num_experts));
   L.total = o;
   return L;
 }
@@ -113,9 +119,18 @@ int moe_w4a16_align_capacity(const moe_w4a16_problem* p, int32_t block_m,
   return MOE_OK;
 }
 
+int moe_w4a16_align_scratch_size(const moe_w4a16_problem* p, size_t* bytes) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = 4 * (size_t)moe::align_scratch_ints(p->num_tokens * p->top_k, p->num_experts);
+  return MOE_OK;
+}
+
 int moe_w4a16_align(const int32_t* topk_ids, const moe_w4a16_problem* p, int32_t block_m,
                     int32_t* sorted_ids, int64_t sorted_cap, int32_t* block_expert,
-                    int64_t block_cap, int32_t* n_padded, void* stream) {
+                    int64_t block_cap, int32_t* n_padded, void* scratch, size_t scratch_bytes,
+                    void* stream) {
   const int st = check_problem(p);
   if (st != MOE_OK) return st;
   if (block_m < 1 || block_m > 1024) return MOE_ERR_SHAPE;
@@ -126,9 +141,17 @@ int moe_w4a16_align(const int32_t* topk_ids, const moe_w4a16_problem* p, int32_t
       !aligned16(n_padded))
     return MOE_ERR_ALIGNMENT;
   if (sorted_cap < need || block_cap < need / block_m) return MOE_ERR_WORKSPACE;
-  return hip_status(moe::launch_align(topk_ids, p->num_tokens * p->top_k, p->num_experts,
-                                      p->expert_base, block_m, sorted_ids, block_expert,
-                                      n_padded, (hipStream_t)stream));
+  const int64_t P = p->num_tokens * p->top_k;
+  if (scratch) {
+    if (!aligned16(scratch)) return MOE_ERR_ALIGNMENT;
+    if (scratch_bytes < 4 * (size_t)moe::align_scratch_ints(P, p->num_experts))
+      return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_align_multi(topk_ids, P, p->num_experts, p->expert_base,
+                                              block_m, sorted_ids, block_expert, n_padded,
+                                              static_cast<int32_t*>(scratch), (hipStream_t)stream));
+  }
+  return hip_status(moe::launch_align(topk_ids, P, p->num_experts, p->expert_base, block_m,
+                                      sorted_ids, block_expert, n_padded, (hipStream_t)stream));
 }
 
 static int forward_impl(const void* x, const int32_t* topk_ids, const float* topk_weights,
@@ -169,8 +192,11 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   };
   hipError_t err = mark(0);
   if (err != hipSuccess) return hip_status(err);
-  err = moe::launch_align(topk_ids, T * k, E, p->expert_base, L.bm, sorted, blk,
-                                     n_padded, strm);
+  if (T * k >= kAlignMultiMin)
+    err = moe::launch_align_multi(topk_ids, T * k, E, p->expert_base, L.bm, sorted, blk, n_padded,
+                                  reinterpret_cast<int32_t*>(ws + L.align_scratch), strm);
+  else
+    err = moe::launch_align(topk_ids, T * k, E, p->expert_base, L.bm, sorted, blk, n_padded, strm);
   if (err != hipSuccess) return hip_status(err);
 
   // One GEMM phase. Prefill blocks: the routed experts in the prefill kernel,

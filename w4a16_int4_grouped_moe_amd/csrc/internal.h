@@ -8,10 +8,16 @@
 namespace moe {
 
 // Bucketing: stable counting sort of valid (token, slot) pairs by local expert.
-// One work-group; E <= 1024.
+// launch_align: one work-group; E <= 1024. launch_align_multi: the same result
+// from many work-groups (three launches), with align_scratch_ints(P, E) int32
+// of scratch.
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* n_padded, hipStream_t stream);
+int64_t align_scratch_ints(int64_t P, int32_t E);
+hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
+                              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                              int32_t* n_padded, int32_t* scratch, hipStream_t stream);
 
 // Operands of one grouped-GEMM launch (routed blocks followed by shared-expert
 // row tiles). Widths are in elements.
