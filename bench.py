@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the W4A16 INT4 grouped MoE layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|skew|ep|tiny]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode|prefill|skew|ep|tp8_decode|tp8_prefill|tiny]
 
 Default workload (the one the metric is quoted on): one Kimi-K2.6-shape MoE
 layer (hidden 7168, moe_intermediate 2048, 384 int4 group-32 experts, top-8,
@@ -157,7 +158,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "skew", "ep", "tiny"])
+                    choices=["decode", "prefill", "skew", "ep", "tp8_decode", "tp8_prefill",
+                             "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens per batch of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -179,7 +181,7 @@ def main():
 
     dev = torch.device("cuda:0")
     hip = Hip()
-    if args.workload == "decode":
+    if args.workload in ("decode", "tp8_decode"):
         batches = [1, 8, 32, 64]
     else:
         batches = [mi.workload(args.workload).T]
@@ -281,7 +283,7 @@ def main():
     traffic = None
     if rec is not None:
         traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-    if args.workload in ("prefill",):
+    if args.workload in ("prefill", "tp8_prefill"):
         ach = float(np.mean(gate_up_flops)) / mean_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
@@ -318,6 +320,10 @@ def main():
     if args.workload == "decode":
         wl = ("Kimi-K2.6-shape W4A16 MoE layer decode: hidden 7168, moe_intermediate 2048, "
               "384 int4 g32 experts, top-8, bf16 shared expert; batches 1/8/32/64 tokens")
+    elif args.workload.startswith("tp8"):
+        wl = ("one GPU's share of the Kimi-K2.6-shape W4A16 MoE layer under 8-way tensor "
+              "parallelism: hidden 7168, moe_intermediate 256, 384 int4 g32 experts, top-8, "
+              f"bf16 shared expert (intermediate 256); batches {'/'.join(map(str, batches))}")
     else:
         wl = f"Kimi-K2.6-shape W4A16 MoE layer, {args.workload} workload, T={batches[0]}"
     line = {

@@ -92,6 +92,10 @@ class Geometry:
 # one shared expert, moe_intermediate_size 2048 (catalog entry, GEOMETRY / MoE).
 KIMI = Geometry(hidden=7168, inter=2048, n_experts=384, top_k=8, shared=True)
 TINY = Geometry(hidden=256, inter=128, n_experts=8, top_k=2, shared=False)
+# one GPU's share of the same layer split 8 ways by tensor parallelism: every
+# expert (and the shared expert) keeps all 7168 inputs and outputs but only
+# 2048 / 8 = 256 intermediate columns (8 whole scale groups)
+TP8_SHARE = Geometry(hidden=7168, inter=256, n_experts=384, top_k=8, shared=True)
 
 
 # --------------------------------------------------------------------------
@@ -201,6 +205,31 @@ def routing_zipf(seed: int, T: int, n_experts: int, k: int, s: float = 1.2):
 
 
 # --------------------------------------------------------------------------
+# tensor-parallel shards (slicing only)
+# --------------------------------------------------------------------------
+def tp_shard(bank: Bank, shared_w: Optional[np.ndarray], hidden: int, inter: int,
+             rank: int, n: int):
+    """Rank `rank` of an n-way split of the intermediate dimension: gate rows
+    and up rows [rank*I/n, (rank+1)*I/n) of W13 (with their scales), the same
+    input columns of W2 (packed words and scale groups), and the same cut of
+    the shared expert. I/n must be a whole number of scale groups."""
+    Is = inter // n
+    assert Is * n == inter and Is % GROUP == 0
+    lo, hi = rank * Is, (rank + 1) * Is
+    rows = np.r_[lo:hi, inter + lo:inter + hi]
+    b = Bank(np.ascontiguousarray(bank.packed_w13[:, rows]),
+             np.ascontiguousarray(bank.scales_w13[:, rows]),
+             np.ascontiguousarray(bank.packed_w2[:, :, lo // 8:hi // 8]),
+             np.ascontiguousarray(bank.scales_w2[:, :, lo // GROUP:hi // GROUP]))
+    sh = None
+    if shared_w is not None:
+        gu = shared_w[:2 * inter * hidden].reshape(2 * inter, hidden)
+        dn = shared_w[2 * inter * hidden:].reshape(hidden, inter)
+        sh = np.concatenate([gu[rows].ravel(), dn[:, lo:hi].ravel()])
+    return b, sh
+
+
+# --------------------------------------------------------------------------
 # crafted bit patterns for invariant tests (no arithmetic of the layer)
 # --------------------------------------------------------------------------
 def const_code_word(code: int) -> np.int32:
@@ -238,6 +267,11 @@ def workload(name: str, T: Optional[int] = None) -> Workload:
     skew     same layer, 512 tokens, Zipf(1.2) routing
     ep       48 local experts (global ids 0..47) of the same bank, 2048 tokens
              routed uniformly over all 384; only local pairs are computed
+    tp8_decode   one GPU's share of the layer under 8-way tensor parallelism
+             (moe_intermediate 256 per expert and for the shared expert),
+             T in {1, 8, 32, 64}; an independent bank (seed 2) with the same
+             value distributions, routing identical to `decode`
+    tp8_prefill  the same share at 4096 tokens, routing identical to `prefill`
     """
     if name == "tiny":
         return Workload("tiny", TINY, T or 16, 8, 0, "uniform", seed_bank=5)
@@ -249,6 +283,10 @@ def workload(name: str, T: Optional[int] = None) -> Workload:
         return Workload("skew", KIMI, T or 512, 384, 0, "zipf")
     if name == "ep":
         return Workload("ep", KIMI, T or 2048, 48, 0, "uniform")
+    if name == "tp8_decode":
+        return Workload("tp8_decode", TP8_SHARE, T or 64, 384, 0, "uniform", seed_bank=2)
+    if name == "tp8_prefill":
+        return Workload("tp8_prefill", TP8_SHARE, T or 4096, 384, 0, "uniform", seed_bank=2)
     raise ValueError(f"unknown workload {name!r}")
 
 

@@ -65,6 +65,9 @@ def test_workspace_size_and_block_m(lib):
     assert moe.forward_block_m(P(num_tokens=4096)) == 96
     assert moe.forward_block_m(P(num_tokens=4096, hidden=7040)) == 64  # 7040 % 256 != 0
     assert moe.forward_block_m(P(num_tokens=2048)) == 64
+    # one GPU's share of an 8-way tensor-parallel split (intermediate 256)
+    assert moe.forward_block_m(P(inter=256)) == 4
+    assert moe.forward_block_m(P(inter=256, num_tokens=4096)) == 96
     n = moe.workspace_size(p)
     T, H, I, k = 64, 7168, 2048, 8
     cap = T * k + min(384, T * k) * 3

@@ -142,3 +142,28 @@ def test_kimi_skew_sampled(dev, kimi):
 
 def test_kimi_expert_parallel_share_sampled(dev, kimi):
     _kimi_case(dev, kimi, "ep", 2048, n_sample=12)
+
+
+# ------------------------------------- 8-way tensor-parallel share (I = 256)
+@pytest.fixture(scope="module")
+def tp8(dev):
+    w = mi.workload("tp8_decode")
+    g = w.geo
+    print("[fixture] generating the 384-expert I=256 bank on the device", flush=True)
+    bank = mi.device_bank(w.seed_bank, g.hidden, g.inter, list(range(g.n_experts)), dev)
+    shared = mi.shared_weights(w.seed_bank, g.hidden, g.inter)
+    return bank, shared
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_tp8_share_decode(dev, tp8, T):
+    _kimi_case(dev, tp8, "tp8_decode", T)
+
+
+def test_tp8_share_prefill_sampled(dev, tp8):
+    import w4a16_int4_grouped_moe_amd as moe
+
+    g = mi.TP8_SHARE
+    print(f"[case] tp8_prefill block_m "
+          f"{moe.forward_block_m(moe.problem(4096, g.hidden, g.inter, 384, 8, 0))}", flush=True)
+    _kimi_case(dev, tp8, "tp8_prefill", 4096, n_sample=12)

@@ -19,6 +19,8 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 MUTANTS = {
     "gate_up_swapped": ("h[i] = silu(a[i]) * a[I + i];", "h[i] = silu(a[I + i]) * a[i];", 2),
+    "gate_up_interleaved": ("h[i] = silu(a[i]) * a[I + i];",
+                            "h[i] = silu(a[2 * i]) * a[2 * i + 1];", 2),
     "twos_complement_codes": ("return field - 8;", "return (field ^ 8) - 8;", 1),
     "high_nibble_first": ("(word >> (4 * (c % 8)))", "(word >> (4 * (7 - c % 8)))", 1),
     "scale_group_reversed": ("scales[n * (C / GROUP) + c / GROUP]",
@@ -46,6 +48,7 @@ PIN_TESTS = [
     lambda: pins.test_dense_formulation_agrees(
         None, dict(seed=33, T=6, H=64, I=32, E=3, k=4, shared=True, base=2, n_global=8)),
     lambda: pins.test_doubling_down_scales_doubles_routed_part(None),
+    lambda: pins.test_tensor_parallel_shards_sum_to_full(None, 2),
 ]
 
 

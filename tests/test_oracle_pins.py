@@ -283,6 +283,30 @@ def test_doubling_down_scales_doubles_routed_part(oracle_lib):
                                atol=1e-12 * np.abs(base).max())
 
 
+@pytest.mark.parametrize("n", [2, 4])
+def test_tensor_parallel_shards_sum_to_full(oracle_lib, n):
+    """SwiGLU acts column by column on the intermediate dimension and the
+    down projection is linear in it, so splitting the intermediate columns of
+    every expert and of the shared expert n ways (gate and up rows, W2 input
+    columns and their scale groups) and adding the n partial layers gives the
+    whole layer: the one-GPU share of a tensor-parallel deployment."""
+    H, I = 64, 128
+    d = _tiny_inputs(seed=46, T=5, H=H, I=I, E=4, k=3, shared=True)
+    bank = mi.Bank(d["packed_w13"], d["scales_w13"], d["packed_w2"], d["scales_w2"])
+    full = oracle.forward(d["x"], d["topk_ids"], d["topk_weights"], d["packed_w13"],
+                          d["scales_w13"], d["packed_w2"], d["scales_w2"], d["shared_w"])
+    acc = np.zeros_like(full)
+    for r in range(n):
+        b, sh = mi.tp_shard(bank, d["shared_w"], H, I, r, n)
+        assert b.packed_w13.shape == (4, 2 * I // n, H // 8)
+        assert b.scales_w2.shape == (4, H, I // n // 32)
+        part = oracle.forward(d["x"], d["topk_ids"], d["topk_weights"], b.packed_w13,
+                              b.scales_w13, b.packed_w2, b.scales_w2, sh)
+        assert np.abs(part).max() > 0
+        acc += part
+    np.testing.assert_allclose(acc, full, rtol=1e-11, atol=1e-12 * np.abs(full).max())
+
+
 def test_token_subset_matches_full(oracle_lib):
     d = _tiny_inputs(seed=45, T=9, H=64, I=32, E=4, k=2, shared=True)
     args = (d["x"], d["topk_ids"], d["topk_weights"], d["packed_w13"], d["scales_w13"],

@@ -512,6 +512,279 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kerne
   }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow reductions (down projection with I <= 512, e.g. one GPU's share of a
+// tensor-parallel split). The whole of K (at most 16 groups) fits in one MFMA
+// instruction's 16 blocks, so K is no longer the streamed dimension: each lane
+// loads its activations once (registers, no LDS, no barrier), and the waves
+// stream weight rows instead, the next step's rows in flight while the current
+// ones are computed. With KG = 16 / RC blocks per copy, block kp holds group
+// kp % KG of row-set copy kp / KG: one instruction covers RC row-sets of four
+// rows, and the k-parts are summed across the KG blocks of each copy at every
+// step. Groups past K (I = 384) are read out of range, i.e. as zeros.
+// ---------------------------------------------------------------------------
+template <int KG>
+__device__ __forceinline__ float kpart_sum_narrow(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                     0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  if (KG >= 8) v += __shfl_xor(v, 16);
+  if (KG >= 16) v += __shfl_xor(v, 32);
+  return v;
+}
+
+constexpr int kNarrowSteps = 8;  // row steps per work-group
+
+// weight rows of one wave step
+template <int KG, int NR>
+constexpr int narrow_rows() { return 4 * NR * (16 / KG); }
+
+// NB blocks of four rows (routed: one 4-row bucket block; shared: NB blocks of
+// consecutive tokens) against weight rows [n0, n0 + nsteps * kWaves * RW).
+template <int KG, int NR, bool INT4, int NB>
+__device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, int n0,
+                                            int nsteps) {
+  constexpr int RC = 16 / KG;
+  constexpr int RW = narrow_rows<KG, NR>();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kp = lane >> 2;
+  const int j = lane & 3;
+  const int c = kp / KG;
+  const int g = kp % KG;
+  const int K = p.K;
+  const bool gvalid = g < K / 32;
+
+  // ---- activations: group g of token row j, once; (x0..x7) permuted to
+  // (x0,x4,x1,x5 | x2,x6,x3,x7) for the int4 codes' field order --------------
+  const uint16_t* abase = INT4 ? p.a_routed : p.a_shared;
+  const int64_t arows = INT4 ? (int64_t)p.max_blocks * 4 : p.T;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)abase, 0, (int)(arows * K * 2), kBufferFlags);
+  u32x4 xf[NB][4];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    int64_t arow = row0 + 4 * b + j;
+    if (!INT4 && arow >= p.T) arow = p.T - 1;  // never stored
+    const int off = gvalid ? (int)(arow * K + 32 * g) * 2 : kOutOfRange;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 16 * q, 0);
+      if (INT4)
+        v = u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
+                  __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                  __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
+                  __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+      xf[b][q] = v;
+    }
+  }
+
+  // ---- weight rows of this lane: row-set rs, copy c, row j ------------------
+  const int Nw = p.N;
+  const int e = INT4 ? p.block_expert[row0 / 4] : 0;
+  const int64_t r0 = (int64_t)e * Nw;
+  __amdgpu_buffer_rsrc_t wres, sres;
+  if (INT4) {
+    wres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.packed + r0 * (K / 8)), 0,
+                                             Nw * (K / 8) * 4, kBufferFlags);
+    sres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
+                                             Nw * (K / 32) * 2, kBufferFlags);
+  } else {
+    wres = __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
+    sres = wres;
+  }
+  auto row_of = [&](int step, int rs) {
+    return n0 + (step * kWaves + wave) * RW + 4 * (rs * RC + c) + j;
+  };
+  int woff[NR], soff[NR];
+#pragma unroll
+  for (int rs = 0; rs < NR; ++rs) {
+    const int row = row_of(0, rs);
+    woff[rs] = !gvalid ? kOutOfRange : INT4 ? (row * (K / 8) + 4 * g) * 4 : (row * K + 32 * g) * 2;
+    soff[rs] = gvalid ? (row * (K / 32) + g) * 2 : kOutOfRange;
+  }
+  const int wstep = kWaves * RW * (INT4 ? K / 2 : 2 * K);  // bytes per step
+  const int sstep = kWaves * RW * (K / 32) * 2;
+  auto sofs = [&](int step, int bytes) {
+    return uniform(step < nsteps ? step * bytes : kOutOfRange);
+  };
+
+  struct Frag {
+    u32x4 w[NR][INT4 ? 1 : 4];
+    uint32_t s[INT4 ? NR : 1];
+  };
+  auto load = [&](Frag& f, int step) {
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) {
+      if (INT4) {
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], sofs(step, wstep), 0);
+        f.s[rs] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rs], sofs(step, sstep), 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          f.w[rs][q] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs] + 16 * q,
+                                                             sofs(step, wstep), 0);
+      }
+    }
+  };
+
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+  if (INT4) {
+    const u32x2 neg136 = {kNeg136, kNeg136};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c0 = mfma4(u32x2{xf[0][q][0], xf[0][q][1]}, neg136, c0);
+      c0 = mfma4(u32x2{xf[0][q][2], xf[0][q][3]}, neg136, c0);
+    }
+  }
+
+  // lane (g, j) of copy c stores token row g % 4 of row-sets g / 4 + (KG / 4) t
+  constexpr int kStores = (NR * 4 + KG - 1) / KG;
+  const int r = g & 3;
+  int32_t pair = 0;
+  if (INT4) pair = p.sorted_ids[row0 + r];
+
+  auto compute_store = [&](const Frag& f, int step) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      f32x4 v[NR];
+      if (INT4) {
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) v[rs] = c0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u32x2 b0[NR], b1[NR];
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs) {
+            const uint32_t w = f.w[rs][0][q];
+            b0[rs] = u32x2{and_or(w, 0x000F000Fu, kMagic), and_or(w >> 4, 0x000F000Fu, kMagic)};
+            b1[rs] = u32x2{and_or(w >> 8, 0x000F000Fu, kMagic),
+                           and_or(w >> 12, 0x000F000Fu, kMagic)};
+          }
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs)
+            v[rs] = mfma4(u32x2{xf[0][q][0], xf[0][q][1]}, b0[rs], v[rs]);
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs)
+            v[rs] = mfma4(u32x2{xf[0][q][2], xf[0][q][3]}, b1[rs], v[rs]);
+        }
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) v[rs] *= bf16_to_f32(f.s[rs]);
+      } else {
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) v[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs)
+            v[rs] = mfma4(u32x2{xf[b][q][0], xf[b][q][1]}, u32x2{f.w[rs][q][0], f.w[rs][q][1]},
+                          v[rs]);
+#pragma unroll
+          for (int rs = 0; rs < NR; ++rs)
+            v[rs] = mfma4(u32x2{xf[b][q][2], xf[b][q][3]}, u32x2{f.w[rs][q][2], f.w[rs][q][3]},
+                          v[rs]);
+        }
+      }
+#pragma unroll
+      for (int rs = 0; rs < NR; ++rs)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[rs][i] = kpart_sum_narrow<KG>(v[rs][i]);
+
+      float* dst = nullptr;
+      if (INT4) {
+        if (pair < p.P) dst = p.y_routed + (int64_t)pair * p.N;
+      } else {
+        const int64_t tok = row0 + 4 * b + r;
+        if (tok < p.T) dst = p.y_shared + tok * p.N;
+      }
+#pragma unroll
+      for (int t = 0; t < kStores; ++t) {
+        const int rsd = (g >> 2) + (KG / 4) * t;
+        if (rsd >= NR) continue;
+        float val = 0.f;
+#pragma unroll
+        for (int rs = 0; rs < NR; ++rs) {
+          if (rs == rsd) {
+            val = v[rs][0];
+            val = (r == 1) ? v[rs][1] : val;
+            val = (r == 2) ? v[rs][2] : val;
+            val = (r == 3) ? v[rs][3] : val;
+          }
+        }
+        if (dst) dst[row_of(step, rsd)] = val;
+      }
+    }
+  };
+
+  Frag fa, fb;
+  load(fa, 0);
+  for (int step = 0; step < nsteps; step += 2) {
+    load(fb, step + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_store(fa, step);
+    if (step + 1 >= nsteps) break;
+    load(fa, step + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_store(fb, step + 1);
+  }
+}
+
+// Work-groups: shared-expert items first (kTokBlocks 4-token blocks each),
+// then routed 4-row bucket blocks; each takes kNarrowSteps wave steps of
+// consecutive weight rows.
+template <int KG, int NR, int NRS>
+__global__ __launch_bounds__(kThreads, 4) void narrow_down_kernel(GemmParams p) {
+  const int64_t bid = blockIdx.x;
+  constexpr int kRowsWGs = kNarrowSteps * kWaves * narrow_rows<KG, NRS>();
+  constexpr int kRowsWG = kNarrowSteps * kWaves * narrow_rows<KG, NR>();
+  const int cs = (p.N + kRowsWGs - 1) / kRowsWGs;
+  const int64_t shared = p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) * cs : 0;
+  if (bid < shared) {
+    const int64_t tg = bid / cs;
+    const int n0 = (int)(bid - tg * cs) * kRowsWGs;
+    const int nsteps = min(kNarrowSteps, (p.N - n0) / (kWaves * narrow_rows<KG, NRS>()));
+    narrow_tile<KG, NRS, false, kTokBlocks>(p, tg * 4 * kTokBlocks, n0, nsteps);
+  } else {
+    const int cr = (p.N + kRowsWG - 1) / kRowsWG;
+    const int64_t b2 = bid - shared;
+    const int64_t blk = b2 / cr;
+    const int n0 = (int)(b2 - blk * cr) * kRowsWG;
+    if (blk * 4 >= *p.n_padded) return;
+    const int nsteps = min(kNarrowSteps, (p.N - n0) / (kWaves * narrow_rows<KG, NR>()));
+    narrow_tile<KG, NR, true, 1>(p, blk * 4, n0, nsteps);
+  }
+}
+
+#ifndef MOE_NARROW_NR
+#define MOE_NARROW_NR 4
+#endif
+#ifndef MOE_NARROW_NRS
+#define MOE_NARROW_NRS 2
+#endif
+
+template <int KG>
+hipError_t launch_narrow(const GemmParams& p, hipStream_t stream) {
+  constexpr int NR = MOE_NARROW_NR, NRS = MOE_NARROW_NRS;
+  // whole wave steps only
+  if (p.N % (kWaves * narrow_rows<KG, NR>()) || p.N % (kWaves * narrow_rows<KG, NRS>()) ||
+      p.K > 512 || p.K % 32)
+    return hipErrorInvalidValue;
+  constexpr int kRowsWGs = kNarrowSteps * kWaves * narrow_rows<KG, NRS>();
+  constexpr int kRowsWG = kNarrowSteps * kWaves * narrow_rows<KG, NR>();
+  const int64_t routed = (int64_t)p.max_blocks * ((p.N + kRowsWG - 1) / kRowsWG);
+  const int64_t shared = p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) *
+                                         ((p.N + kRowsWGs - 1) / kRowsWGs)
+                                   : 0;
+  const int64_t grid = routed + shared;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  GemmParams args = p;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&narrow_down_kernel<KG, NR, NRS>),
+                         dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+}
+
 // Dynamic LDS of a launch: two activation stages (of the larger of the routed
 // and the shared work items) and, for the routed ones, the staged scales.
 template <int NR>
@@ -553,6 +826,9 @@ hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_down_small(const GemmParams& p, hipStream_t stream) {
+  if (p.K <= 128) return launch_narrow<4>(p, stream);
+  if (p.K <= 256) return launch_narrow<8>(p, stream);
+  if (p.K <= 512) return launch_narrow<16>(p, stream);
   return launch_small<kDown, kNRDown, kNRS>(p, stream);
 }
 
