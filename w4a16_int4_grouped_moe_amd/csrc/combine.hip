@@ -6,7 +6,8 @@
 // even). The shared expert enters with weight 1 (Kimi-K2.6 catalog entry, MoE
 // paragraph: one always-on shared expert); routing weights are applied as
 // given. One work-group per token and 1024-column slab, four columns per thread
-// (16-byte loads of y and s, 8-byte stores).
+// (16-byte loads of y and s, 8-byte stores); the loads of eight slots are in
+// flight together.
 #include "internal.h"
 
 namespace moe {
@@ -15,6 +16,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
@@ -23,22 +25,61 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+constexpr int kBufferFlags = 0x00020000;       // raw buffer resource, dword 3
+constexpr int kOutOfRange = (int)0x80000000u;  // buffer offset past any resource: reads 0
+constexpr int kSlotBatch = 8;                  // slots whose loads are in flight together
+
+// The loads of slots j0 .. j0 + kSlotBatch - 1 (all of them inside k when
+// FULL: their ids and weights are then read with unconditional scalar loads)
+// are issued before any is used; slots past k or not local read out of range,
+// i.e. zeros (their rows of y were never written), and are skipped.
+template <bool FULL>
+__device__ __forceinline__ void combine_slots(f32x4& acc, __amdgpu_buffer_rsrc_t yres,
+                                              const int32_t* ids, const float* w, int j0, int k,
+                                              int H, int n, int E, int base) {
+  bool ok[kSlotBatch];
+  float wt[kSlotBatch];
+  f32x4 v[kSlotBatch];
+#pragma unroll
+  for (int u = 0; u < kSlotBatch; ++u) {
+    const int j = j0 + u;
+    const bool in = FULL || j < k;
+    const int e = in ? ids[j] - base : -1;
+    ok[u] = (unsigned)e < (unsigned)E;
+    wt[u] = in ? w[j] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kSlotBatch; ++u)
+    v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         yres, ok[u] ? ((j0 + u) * H + n) * 4 : kOutOfRange, 0, 0));
+#pragma unroll
+  for (int u = 0; u < kSlotBatch; ++u) {
+    if (!ok[u]) continue;
+    acc.x = fmaf(wt[u], v[u].x, acc.x);
+    acc.y = fmaf(wt[u], v[u].y, acc.y);
+    acc.z = fmaf(wt[u], v[u].z, acc.z);
+    acc.w = fmaf(wt[u], v[u].w, acc.w);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float* __restrict__ y, const float* __restrict__ s, const int32_t* __restrict__ ids,
     const float* __restrict__ w, uint16_t* __restrict__ out, int H, int k, int E, int base) {
   const int64_t t = blockIdx.x;
   const int n = (blockIdx.y * kThreads + threadIdx.x) * 4;
   if (n >= H) return;
-  f32x4 acc = s ? *reinterpret_cast<const f32x4*>(s + t * H + n) : f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int e = ids[t * k + j] - base;
-    if ((unsigned)e >= (unsigned)E) continue;
-    const float wt = w[t * k + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(y + (t * k + j) * H + n);
-    acc.x = fmaf(wt, v.x, acc.x);
-    acc.y = fmaf(wt, v.y, acc.y);
-    acc.z = fmaf(wt, v.z, acc.z);
-    acc.w = fmaf(wt, v.w, acc.w);
+  // the token's k rows of y are contiguous (row = pair id = t * k + j); without
+  // a shared expert the s resource is empty and reads zeros
+  const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(y + t * k * H), 0, k * H * 4, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(s ? s + t * H : y), 0, s ? H * 4 : 0, kBufferFlags);
+  f32x4 acc = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sres, n * 4, 0, 0));
+  for (int j0 = 0; j0 < k; j0 += kSlotBatch) {
+    if (j0 + kSlotBatch <= k)
+      combine_slots<true>(acc, yres, ids + t * k, w + t * k, j0, k, H, n, E, base);
+    else
+      combine_slots<false>(acc, yres, ids + t * k, w + t * k, j0, k, H, n, E, base);
   }
   uint2 o;
   o.x = pack_bf16x2(acc.x, acc.y);

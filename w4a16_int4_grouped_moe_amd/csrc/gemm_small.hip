@@ -534,7 +534,14 @@ __device__ __forceinline__ float kpart_sum_narrow(float v) {
   return v;
 }
 
-constexpr int kNarrowSteps = 8;  // row steps per work-group
+#ifndef MOE_NARROW_STEPS
+#define MOE_NARROW_STEPS 4
+#endif
+constexpr int kNarrowSteps = MOE_NARROW_STEPS;  // row steps per work-group
+#ifndef MOE_NARROW_DEPTH
+#define MOE_NARROW_DEPTH 3
+#endif
+constexpr int kNarrowDepth = MOE_NARROW_DEPTH;  // int4 steps in flight ahead
 
 // weight rows of one wave step
 template <int KG, int NR>
@@ -542,7 +549,7 @@ constexpr int narrow_rows() { return 4 * NR * (16 / KG); }
 
 // NB blocks of four rows (routed: one 4-row bucket block; shared: NB blocks of
 // consecutive tokens) against weight rows [n0, n0 + nsteps * kWaves * RW).
-template <int KG, int NR, bool INT4, int NB>
+template <int KG, int NR, bool INT4, int NB, int DEPTH>
 __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, int n0,
                                             int nsteps) {
   constexpr int RC = 16 / KG;
@@ -569,16 +576,13 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
     if (!INT4 && arow >= p.T) arow = p.T - 1;  // never stored
     const int off = gvalid ? (int)(arow * K + 32 * g) * 2 : kOutOfRange;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 16 * q, 0);
-      if (INT4)
-        v = u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
-                  __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
-                  __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
-                  __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
-      xf[b][q] = v;
-    }
+    for (int q = 0; q < 4; ++q) xf[b][q] = __builtin_amdgcn_raw_buffer_load_b128(xres, off, 16 * q, 0);
   }
+  // (permuted below, after the first weight loads are issued)
+  // the pair of token row r, read before the weights for the same reason
+  const int r = g & 3;
+  int32_t pair = 0;
+  if (INT4) pair = p.sorted_ids[row0 + r];
 
   // ---- weight rows of this lane: row-set rs, copy c, row j ------------------
   const int Nw = p.N;
@@ -629,8 +633,27 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
     }
   };
 
+  // ring of DEPTH + 1 register stages: the loads of DEPTH steps are in flight
+  // while a step is computed (past nsteps they read out of range: no traffic)
+  Frag f[DEPTH + 1];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    load(f[d], d);
+    // keep the steps' loads in issue order, so that a step waits for its own
+    // loads only
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
   if (INT4) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = xf[0][q];
+      xf[0][q] = u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
+                       __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                       __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
+                       __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+    }
     const u32x2 neg136 = {kNeg136, kNeg136};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -641,9 +664,6 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
 
   // lane (g, j) of copy c stores token row g % 4 of row-sets g / 4 + (KG / 4) t
   constexpr int kStores = (NR * 4 + KG - 1) / KG;
-  const int r = g & 3;
-  int32_t pair = 0;
-  if (INT4) pair = p.sorted_ids[row0 + r];
 
   auto compute_store = [&](const Frag& f, int step) {
 #pragma unroll
@@ -717,16 +737,12 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
     }
   };
 
-  Frag fa, fb;
-  load(fa, 0);
-  for (int step = 0; step < nsteps; step += 2) {
-    load(fb, step + 1);
+#pragma unroll
+  for (int step = 0; step < kNarrowSteps; ++step) {
+    if (step >= nsteps) break;
+    if (step + DEPTH < kNarrowSteps) load(f[(step + DEPTH) % (DEPTH + 1)], step + DEPTH);
     __builtin_amdgcn_sched_barrier(0);
-    compute_store(fa, step);
-    if (step + 1 >= nsteps) break;
-    load(fa, step + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_store(fb, step + 1);
+    compute_store(f[step % (DEPTH + 1)], step);
   }
 }
 
@@ -734,7 +750,10 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
 // then routed 4-row bucket blocks; each takes kNarrowSteps wave steps of
 // consecutive weight rows.
 template <int KG, int NR, int NRS>
-__global__ __launch_bounds__(kThreads, 4) void narrow_down_kernel(GemmParams p) {
+#ifndef MOE_NARROW_WAVES
+#define MOE_NARROW_WAVES 3
+#endif
+__global__ __launch_bounds__(kThreads, MOE_NARROW_WAVES) void narrow_down_kernel(GemmParams p) {
   const int64_t bid = blockIdx.x;
   constexpr int kRowsWGs = kNarrowSteps * kWaves * narrow_rows<KG, NRS>();
   constexpr int kRowsWG = kNarrowSteps * kWaves * narrow_rows<KG, NR>();
@@ -744,7 +763,7 @@ __global__ __launch_bounds__(kThreads, 4) void narrow_down_kernel(GemmParams p) 
     const int64_t tg = bid / cs;
     const int n0 = (int)(bid - tg * cs) * kRowsWGs;
     const int nsteps = min(kNarrowSteps, (p.N - n0) / (kWaves * narrow_rows<KG, NRS>()));
-    narrow_tile<KG, NRS, false, kTokBlocks>(p, tg * 4 * kTokBlocks, n0, nsteps);
+    narrow_tile<KG, NRS, false, kTokBlocks, 1>(p, tg * 4 * kTokBlocks, n0, nsteps);
   } else {
     const int cr = (p.N + kRowsWG - 1) / kRowsWG;
     const int64_t b2 = bid - shared;
@@ -752,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 4) void narrow_down_kernel(GemmParams p) 
     const int n0 = (int)(b2 - blk * cr) * kRowsWG;
     if (blk * 4 >= *p.n_padded) return;
     const int nsteps = min(kNarrowSteps, (p.N - n0) / (kWaves * narrow_rows<KG, NR>()));
-    narrow_tile<KG, NR, true, 1>(p, blk * 4, n0, nsteps);
+    narrow_tile<KG, NR, true, 1, kNarrowDepth>(p, blk * 4, n0, nsteps);
   }
 }
 
