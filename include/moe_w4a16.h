@@ -54,6 +54,7 @@ extern "C" {
 
 #define MOE_MAX_TOP_K 16
 #define MOE_MAX_EXPERTS 512
+#define MOE_MAX_SCORED 1024 /* experts scored per token by the router step */
 
 /* Problem sizes (host struct, read during the call only). */
 typedef struct {
@@ -137,10 +138,11 @@ int moe_w4a16_align_scratch_size(const moe_w4a16_problem *p, size_t *bytes);
  *   out          bf16  [T, H], fully overwritten; must not alias an input
  *   workspace    device scratch of at least moe_w4a16_workspace_size bytes
  *
- * Numerics: bf16 x bf16 matrix products with fp32 accumulation; the
- * dequantised weights and the SwiGLU output h are rounded to bf16 before
- * their products, everything else stays fp32 until the final bf16 rounding
- * (round to nearest even).
+ * Numerics: bf16 x bf16 matrix products with fp32 accumulation. The SwiGLU
+ * output h is rounded to bf16 before the down product; the dequantised
+ * weights are exact in the small-batch kernels (codes in the MFMA, scale
+ * applied in fp32) and rounded to bf16 in the others; everything else stays
+ * fp32 until the final bf16 rounding (round to nearest even).
  */
 int moe_w4a16_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
                       const int32_t *packed_w13, const void *scales_w13,
@@ -165,6 +167,42 @@ int moe_w4a16_forward_timed(const void *x, const int32_t *topk_ids, const float 
                             const void *shared_w, void *out, const moe_w4a16_problem *p,
                             void *workspace, size_t workspace_bytes, void *stream,
                             void *const *stage_events);
+
+/*
+ * The router step in front of the layer. The lmdeploy pull request "support
+ * Kimi K2.6" (Runtime Validation) lists MoE routing among the validated paths
+ * without a formula; the plainest rule is implemented:
+ *
+ *   topk_ids[t]     = the top_k experts with the largest scores[t, :], in
+ *                     descending score order; equal scores in ascending
+ *                     expert id (-0.0 equals +0.0)
+ *   topk_weights[t] = softmax over the selected scores (fp32, largest score
+ *                     subtracted first) -- the softmax over all experts
+ *                     renormalised over the selected ones
+ *
+ *   scores       fp32  [T, num_scored]  one score per expert of the model
+ *                      (global ids 0 .. num_scored-1); must not hold NaN
+ *   topk_ids     int32 [T, k]   written (global ids)
+ *   topk_weights fp32  [T, k]   written
+ *
+ * T and k come from `p` (the whole problem is validated); 1 <= k <=
+ * num_scored <= MOE_MAX_SCORED and expert_base + num_experts <= num_scored,
+ * else MOE_ERR_SHAPE. T == 0 is a no-op.
+ */
+int moe_w4a16_route(const float *scores, int32_t num_scored, const moe_w4a16_problem *p,
+                    int32_t *topk_ids, float *topk_weights, void *stream);
+
+/*
+ * The router step followed by the layer, on `stream`: moe_w4a16_route into
+ * the caller's topk_ids / topk_weights (outputs here), then moe_w4a16_forward
+ * on them, with the same workspace and the same results as the two calls.
+ */
+int moe_w4a16_forward_scores(const void *x, const float *scores, int32_t num_scored,
+                             const int32_t *packed_w13, const void *scales_w13,
+                             const int32_t *packed_w2, const void *scales_w2,
+                             const void *shared_w, void *out, int32_t *topk_ids,
+                             float *topk_weights, const moe_w4a16_problem *p, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /*
  * A static description of `status`; for MOE_ERR_HIP it names the HIP error

@@ -45,6 +45,7 @@ TAG_SHARED = 7
 TAG_X = 11
 TAG_ROUTE = 17
 TAG_ZIPF_PERM = 19
+TAG_SCORES = 23
 
 SCALE_LO = 0.005
 SCALE_HI = 0.02
@@ -202,6 +203,11 @@ def routing_zipf(seed: int, T: int, n_experts: int, k: int, s: float = 1.2):
     perm = _rng(seed, TAG_ZIPF_PERM).permutation(n_experts)
     ids = perm[top].astype(np.int32)
     return np.ascontiguousarray(ids), _softmax_weights(r, T, k)
+
+
+def router_scores(seed: int, T: int, n_experts: int) -> np.ndarray:
+    """fp32 router scores [T, n_experts], N(0, 1): the input of the router step."""
+    return _rng(seed, TAG_SCORES).standard_normal(size=(T, n_experts), dtype=np.float32)
 
 
 # --------------------------------------------------------------------------

@@ -12,6 +12,7 @@ from .oracle import (  # noqa: F401
     forward,
     int4_code_c,
     pack_int4,
+    route,
     silu_c,
     unpack_int4,
 )

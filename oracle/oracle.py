@@ -14,6 +14,8 @@ Contents
   align        the token/expert bucketing: a stable sort of the valid
                (token, slot) pairs by local expert, each bucket padded to a
                multiple of block_m with the sentinel T*k.
+  route        the router step in front of the layer: top-k experts per
+               token from fp32 scores, weights = softmax over the selected.
 
 Readings of the pages (Kimi-K2.6 catalog entry: QUANT paragraph -- INT4,
 compressed-tensors pack-quantized, group 32, symmetric; PARAMS paragraph --
@@ -230,3 +232,26 @@ def align(topk_ids, num_experts: int, expert_base: int, block_m: int):
     sorted_ids[off[e_sorted] + rank] = p_sorted
     block_expert = np.repeat(np.arange(num_experts, dtype=np.int32), pad // block_m)
     return sorted_ids, block_expert, n_padded
+
+
+def route(scores, top_k: int):
+    """The router step that produces the layer's routing inputs.
+
+    The lmdeploy pull request (Runtime Validation) lists MoE routing among the
+    validated paths without giving a formula; the plainest rule, the one the
+    synthetic inputs follow, is taken: for each token the top_k experts with
+    the largest scores, in descending score order, equal scores in ascending
+    expert id (-0.0 equals +0.0); weights = softmax over the selected scores,
+    which is the softmax over all experts renormalised over the selected ones.
+    Selection compares the fp32 scores as given; the weights are computed in
+    fp64. Scores must not be NaN.
+
+    Returns (ids int32 [T, top_k], weights float64 [T, top_k]).
+    """
+    s = np.asarray(scores, np.float32).astype(np.float64)
+    T, E = s.shape
+    assert 1 <= top_k <= E
+    ids = np.argsort(-s, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    z = np.exp(sel - sel[:, :1])  # the first selected score is the largest
+    return ids, z / z.sum(axis=1, keepdims=True)

@@ -32,8 +32,8 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_align_scratch_size",
         "moe_w4a16_forward",
-        "moe_w4a16_forward_block_m", "moe_w4a16_forward_timed", "moe_w4a16_status_string",
-        "moe_w4a16_workspace_size"])
+        "moe_w4a16_forward_block_m", "moe_w4a16_forward_scores", "moe_w4a16_forward_timed",
+        "moe_w4a16_route", "moe_w4a16_status_string", "moe_w4a16_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -49,6 +49,11 @@ def test_status_codes_match_header(lib):
         m = re.search(r"#define %s \(?(-?\d+)\)?" % name, text)
         assert m and int(m.group(1)) == getattr(moe, name), name
         assert moe.status_string(getattr(moe, name)).startswith(name)
+    from w4a16_int4_grouped_moe_amd import _binding
+
+    for name in ["MOE_MAX_EXPERTS", "MOE_MAX_SCORED"]:
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(_binding, name), name
 
 
 def P(**kw):
@@ -168,3 +173,36 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.library()
+
+
+def test_route_argument_errors(lib):
+    f = ctypes.c_void_p
+    sc, ids, w = f(0x10000), f(0x20000), f(0x30000)
+
+    def call(S=384, p=None, **over):
+        a = dict(sc=sc, ids=ids, w=w)
+        a.update(over)
+        return lib.moe_w4a16_route(a["sc"], S, ctypes.byref(p or P()), a["ids"], a["w"], None)
+
+    assert call(S=0) == moe.MOE_ERR_SHAPE
+    assert call(S=1025) == moe.MOE_ERR_SHAPE
+    assert call(S=7) == moe.MOE_ERR_SHAPE                      # top_k 8 > 7 scores
+    assert call(S=383) == moe.MOE_ERR_SHAPE                    # local experts beyond the scores
+    assert call(p=P(num_experts=48, expert_base=340)) == moe.MOE_ERR_SHAPE
+    assert call(p=P(hidden=7100)) == moe.MOE_ERR_SHAPE          # the whole problem is checked
+    assert call(sc=None) == moe.MOE_ERR_NULL
+    assert call(ids=None) == moe.MOE_ERR_NULL
+    assert call(w=f(0x30004)) == moe.MOE_ERR_ALIGNMENT
+    assert call(p=P(num_tokens=0), sc=None, ids=None, w=None) == moe.MOE_OK  # no-op
+    # the combined call checks the layer's arguments before its first launch
+    good = [f(0x40000 + 0x100 * i) for i in range(7)]
+    p = P()
+    need = moe.workspace_size(p)
+    args = [good[0], sc, 384] + good[1:7] + [ids, w, ctypes.byref(p), f(0x50000)]
+    assert lib.moe_w4a16_forward_scores(*args, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    bad = list(args)
+    bad[0] = None
+    assert lib.moe_w4a16_forward_scores(*bad, need, None) == moe.MOE_ERR_NULL
+    bad = list(args)
+    bad[2] = 2000
+    assert lib.moe_w4a16_forward_scores(*bad, need, None) == moe.MOE_ERR_SHAPE

@@ -372,3 +372,93 @@ def test_workload_routing_shapes():
     assert all(len(set(r)) == 8 for r in zi.tolist())
     counts = np.bincount(zi.ravel(), minlength=384)
     assert counts.max() > 300 and (counts == 0).sum() > 10  # heavy skew, idle experts
+
+
+# --------------------------------------------------------------------------
+# router step (top-k + softmax over the selected)
+# --------------------------------------------------------------------------
+def _route_case(scores, k):
+    return oracle.route(np.array([scores], np.float32), k)
+
+
+def test_route_hand_examples():
+    e = math.e
+    ids, w = _route_case([1.0, 3.0, 2.0, 0.5], 2)  # top two: 3 and 2, one apart
+    assert ids.tolist() == [[1, 2]]
+    np.testing.assert_allclose(w[0], [e / (e + 1), 1 / (e + 1)], rtol=1e-15)
+    # ties go to the lower expert id, and the selection keeps descending order
+    ids, w = _route_case([2.0, 5.0, 2.0, 5.0, 2.0], 3)
+    assert ids.tolist() == [[1, 3, 0]]
+    d = 2 + math.exp(-3)
+    np.testing.assert_allclose(w[0], [1 / d, 1 / d, math.exp(-3) / d], rtol=1e-15)
+    # -0.0 and +0.0 are equal scores
+    ids, w = _route_case([-0.0, 0.0, -1.0], 2)
+    assert ids.tolist() == [[0, 1]] and w.tolist() == [[0.5, 0.5]]
+    ids, w = _route_case([-0.0, -1.0, 0.0], 2)
+    assert ids.tolist() == [[0, 2]]
+    # equal scores: the first k experts, equal weights
+    ids, w = _route_case([0.25] * 6, 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] and w.tolist() == [[0.25] * 4]
+    # large magnitudes: only differences matter
+    ids, w = _route_case([-100.0, -101.0, -99.0], 2)
+    assert ids.tolist() == [[2, 0]]
+    np.testing.assert_allclose(w[0], [e / (e + 1), 1 / (e + 1)], rtol=1e-13)
+    # k = E: every expert, sorted
+    ids, w = _route_case([0.0, 2.0, 1.0], 3)
+    assert ids.tolist() == [[1, 2, 0]]
+    np.testing.assert_allclose(w[0], np.array([e * e, e, 1.0]) / (e * e + e + 1), rtol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_brute_force(seed):
+    """Against an exhaustive search: the selected set is the k-subset with the
+    largest score sum, the lexicographically smallest id tuple among equal
+    sums, listed by descending score then id."""
+    import itertools
+
+    rng = np.random.default_rng(seed)
+    E, k, T = int(rng.integers(1, 8)), 0, 5
+    k = int(rng.integers(1, E + 1))
+    scores = rng.integers(-2, 3, size=(T, E)).astype(np.float32)  # many ties
+    scores[:, :: 3] *= np.float32(0.5)
+    ids, w = oracle.route(scores, k)
+    for t in range(T):
+        s = scores[t].astype(np.float64)
+        best = max(itertools.combinations(range(E), k),
+                   key=lambda c: (sum(s[list(c)]), tuple(-i for i in c)))
+        want = sorted(best, key=lambda e: (-s[e], e))
+        assert ids[t].tolist() == want, (t, scores[t], ids[t], want)
+        z = np.exp(s[want] - s[want].max())
+        np.testing.assert_allclose(w[t], z / z.sum(), rtol=1e-14)
+
+
+def test_route_equals_renormalised_full_softmax():
+    from scipy.special import softmax
+
+    rng = np.random.default_rng(3)
+    scores = rng.standard_normal((7, 384)).astype(np.float32)
+    ids, w = oracle.route(scores, 8)
+    p = softmax(scores.astype(np.float64), axis=1)
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-12)
+    # every unselected score is at most the smallest selected one
+    for t in range(7):
+        rest = np.setdiff1d(np.arange(384), ids[t])
+        assert scores[t, rest].max() <= scores[t, ids[t]].min()
+        assert np.all(np.diff(scores[t, ids[t]]) <= 0)
+
+
+def test_route_shift_and_permutation():
+    rng = np.random.default_rng(4)
+    scores = rng.integers(-50, 50, size=(6, 40)).astype(np.float32)  # exact under shifts
+    ids, w = oracle.route(scores, 6)
+    ids2, w2 = oracle.route(scores + np.float32(1000), 6)
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_allclose(w, w2, rtol=1e-14)
+    d = rng.permutation(40 * 6).reshape(6, 40).astype(np.float32)  # distinct scores
+    perm = rng.permutation(40)  # new column perm[e] holds old expert e
+    moved = np.empty_like(d)
+    moved[:, perm] = d
+    a, wa = oracle.route(d, 5)
+    b, wb = oracle.route(moved, 5)
+    assert np.array_equal(perm[a], b) and np.array_equal(wa, wb)

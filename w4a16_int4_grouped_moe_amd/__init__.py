@@ -6,6 +6,8 @@ PyTorch supplies device memory and the current stream.
 
     out = forward(x, topk_ids, topk_weights, packed_w13, scales_w13,
                   packed_w2, scales_w2, shared_w=None, out=None, expert_base=0)
+    ids, weights = route(scores, top_k)              # router step
+    out, ids, weights = forward_scores(x, scores, top_k, packed_w13, ...)
 """
 from ._binding import (  # noqa: F401
     MOE_ERR_ALIGNMENT,
@@ -23,8 +25,10 @@ from ._binding import (  # noqa: F401
     align_scratch_size,
     forward,
     forward_block_m,
+    forward_scores,
     library,
     problem,
+    route,
     status_string,
     workspace_size,
 )

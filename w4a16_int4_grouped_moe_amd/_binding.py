@@ -15,6 +15,8 @@ MOE_ERR_ALIGNMENT = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_UNSUPPORTED = -5
 MOE_ERR_HIP = -6
+MOE_MAX_EXPERTS = 512
+MOE_MAX_SCORED = 1024
 
 GROUP = 32
 
@@ -61,10 +63,14 @@ def library():
         lib.moe_w4a16_align_scratch_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_w4a16_forward.argtypes = [P] * 9 + [PP, P, ctypes.c_size_t, P]
         lib.moe_w4a16_forward_timed.argtypes = [P] * 9 + [PP, P, ctypes.c_size_t, P, P]
+        lib.moe_w4a16_route.argtypes = [P, ctypes.c_int32, PP, P, P, P]
+        lib.moe_w4a16_forward_scores.argtypes = ([P, P, ctypes.c_int32] + [P] * 8 +
+                                                 [PP, P, ctypes.c_size_t, P])
         lib.moe_w4a16_status_string.argtypes = [ctypes.c_int]
         lib.moe_w4a16_status_string.restype = ctypes.c_char_p
         for f in ("workspace_size", "forward_block_m", "align_capacity", "align",
-                  "align_scratch_size", "forward", "forward_timed"):
+                  "align_scratch_size", "forward", "forward_timed", "route",
+                  "forward_scores"):
             getattr(lib, "moe_w4a16_" + f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -131,27 +137,15 @@ def _need(t, name, dtype, ndim, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
-            shared_w=None, out=None, expert_base: int = 0, workspace=None,
-            stage_events=None):
-    """The W4A16 MoE layer (see include/moe_w4a16.h for the definition).
-
-    x bf16 [T, H]; topk_ids int32 [T, k]; topk_weights fp32 [T, k];
-    packed_w13 int32 [E, 2I, H/8]; scales_w13 bf16 [E, 2I, H/32];
-    packed_w2 int32 [E, H, I/8]; scales_w2 bf16 [E, H, I/32];
-    shared_w bf16 [2I*H + H*I] or None. Returns out bf16 [T, H].
-    stage_events: optional sequence of 7 raw hipEvent_t handles (int or None)
-    recorded between the stages (see moe_w4a16_forward_timed).
-    """
+def _layer(x, k, packed_w13, scales_w13, packed_w2, scales_w2, shared_w, out, expert_base,
+           workspace):
+    """Checks the layer's tensors; returns (problem, out, workspace)."""
     torch = _torch()
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("x must be a GPU tensor")
     _need(x, "x", torch.bfloat16, 2, dev)
     T, H = x.shape
-    _need(topk_ids, "topk_ids", torch.int32, 2, dev)
-    k = topk_ids.shape[1]
-    _need(topk_weights, "topk_weights", torch.float32, 2, dev)
     _need(packed_w13, "packed_w13", torch.int32, 3, dev)
     E, I2, _ = packed_w13.shape
     I = I2 // 2
@@ -159,8 +153,6 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
     _need(packed_w2, "packed_w2", torch.int32, 3, dev)
     _need(scales_w2, "scales_w2", torch.bfloat16, 3, dev)
     shapes = {
-        "topk_ids": (tuple(topk_ids.shape), (T, k)),
-        "topk_weights": (tuple(topk_weights.shape), (T, k)),
         "packed_w13": (tuple(packed_w13.shape), (E, 2 * I, H // 8)),
         "scales_w13": (tuple(scales_w13.shape), (E, 2 * I, H // GROUP)),
         "packed_w2": (tuple(packed_w2.shape), (E, H, I // 8)),
@@ -185,10 +177,45 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, 1, dev)
+    return p, out, workspace
+
+
+def _routing(topk_ids, topk_weights, T, k, dev):
+    torch = _torch()
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, 2, dev)
+    _need(topk_weights, "topk_weights", torch.float32, 2, dev)
+    for name, t in (("topk_ids", topk_ids), ("topk_weights", topk_weights)):
+        if tuple(t.shape) != (T, k):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(T, k)}")
+    return topk_ids, topk_weights
+
+
+def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+            shared_w=None, out=None, expert_base: int = 0, workspace=None,
+            stage_events=None):
+    """The W4A16 MoE layer (see include/moe_w4a16.h for the definition).
+
+    x bf16 [T, H]; topk_ids int32 [T, k]; topk_weights fp32 [T, k];
+    packed_w13 int32 [E, 2I, H/8]; scales_w13 bf16 [E, 2I, H/32];
+    packed_w2 int32 [E, H, I/8]; scales_w2 bf16 [E, H, I/32];
+    shared_w bf16 [2I*H + H*I] or None. Returns out bf16 [T, H].
+    stage_events: optional sequence of 7 raw hipEvent_t handles (int or None)
+    recorded between the stages (see moe_w4a16_forward_timed).
+    """
+    torch = _torch()
+    _need(topk_ids, "topk_ids", torch.int32, 2, x.device)
+    k = topk_ids.shape[1]
+    p, out, workspace = _layer(x, k, packed_w13, scales_w13, packed_w2, scales_w2, shared_w,
+                               out, expert_base, workspace)
+    _routing(topk_ids, topk_weights, x.shape[0], k, x.device)
     args = (x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), packed_w13.data_ptr(),
             scales_w13.data_ptr(), packed_w2.data_ptr(), scales_w2.data_ptr(),
             None if shared_w is None else shared_w.data_ptr(), out.data_ptr(), ctypes.byref(p),
-            workspace.data_ptr(), workspace.numel(), _stream_handle(dev))
+            workspace.data_ptr(), workspace.numel(), _stream_handle(x.device))
     if stage_events is None:
         st = library().moe_w4a16_forward(*args)
     else:
@@ -198,6 +225,48 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
         st = library().moe_w4a16_forward_timed(*args, ev)
     _check(st)
     return out
+
+
+def route(scores, top_k: int, num_experts: Optional[int] = None, expert_base: int = 0,
+          topk_ids=None, topk_weights=None):
+    """The router step (see moe_w4a16_route): scores fp32 [T, S] -> (topk_ids
+    int32 [T, top_k], topk_weights fp32 [T, top_k]). num_experts / expert_base
+    describe the local experts of the layer that follows (default: the first
+    min(S, MOE_MAX_EXPERTS))."""
+    torch = _torch()
+    dev = scores.device
+    _need(scores, "scores", torch.float32, 2, dev)
+    T, S = scores.shape
+    topk_ids, topk_weights = _routing(topk_ids, topk_weights, T, top_k, dev)
+    if num_experts is None:
+        num_experts = min(S, MOE_MAX_EXPERTS)
+    p = problem(T, 128, 128, num_experts, top_k, expert_base)
+    _check(library().moe_w4a16_route(scores.data_ptr(), S, ctypes.byref(p), topk_ids.data_ptr(),
+                                     topk_weights.data_ptr(), _stream_handle(dev)))
+    return topk_ids, topk_weights
+
+
+def forward_scores(x, scores, top_k: int, packed_w13, scales_w13, packed_w2, scales_w2,
+                   shared_w=None, out=None, expert_base: int = 0, workspace=None,
+                   topk_ids=None, topk_weights=None):
+    """The router step followed by the layer (moe_w4a16_forward_scores).
+    Returns (out, topk_ids, topk_weights)."""
+    torch = _torch()
+    _need(scores, "scores", torch.float32, 2, x.device)
+    T, S = scores.shape
+    if T != x.shape[0]:
+        raise ValueError("scores and x must have the same number of tokens")
+    p, out, workspace = _layer(x, top_k, packed_w13, scales_w13, packed_w2, scales_w2,
+                               shared_w, out, expert_base, workspace)
+    topk_ids, topk_weights = _routing(topk_ids, topk_weights, T, top_k, x.device)
+    st = library().moe_w4a16_forward_scores(
+        x.data_ptr(), scores.data_ptr(), S, packed_w13.data_ptr(), scales_w13.data_ptr(),
+        packed_w2.data_ptr(), scales_w2.data_ptr(),
+        None if shared_w is None else shared_w.data_ptr(), out.data_ptr(),
+        topk_ids.data_ptr(), topk_weights.data_ptr(), ctypes.byref(p), workspace.data_ptr(),
+        workspace.numel(), _stream_handle(x.device))
+    _check(st)
+    return out, topk_ids, topk_weights
 
 
 def align_scratch_size(p: Problem) -> int:

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_w4a16.so")
-SOURCES = ["align.hip", "gemm.hip", "gemm_small.hip", "gemm_prefill.hip", "combine.hip", "api.cpp"]
+SOURCES = ["align.hip", "route.hip", "gemm.hip", "gemm_small.hip", "gemm_prefill.hip", "combine.hip",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # packed fp32 VALU forms are disabled for all device code

@@ -154,11 +154,12 @@ int moe_w4a16_align(const int32_t* topk_ids, const moe_w4a16_problem* p, int32_t
                                       sorted_ids, block_expert, n_padded, (hipStream_t)stream));
 }
 
-static int forward_impl(const void* x, const int32_t* topk_ids, const float* topk_weights,
-                        const int32_t* packed_w13, const void* scales_w13,
-                        const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
-                        void* out, const moe_w4a16_problem* p, void* workspace,
-                        size_t workspace_bytes, void* stream, void* const* events) {
+// The layer call's argument checks (before any launch).
+static int check_forward(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                         const int32_t* packed_w13, const void* scales_w13,
+                         const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
+                         const void* out, const moe_w4a16_problem* p, const void* workspace,
+                         size_t workspace_bytes) {
   const int st = check_problem(p);
   if (st != MOE_OK) return st;
   if (p->num_tokens == 0) return MOE_OK;
@@ -169,8 +170,19 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
                         packed_w2, scales_w2, shared_w, out, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return MOE_ERR_ALIGNMENT;
+  if (workspace_bytes < layout(p).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+static int forward_impl(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                        const int32_t* packed_w13, const void* scales_w13,
+                        const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
+                        void* out, const moe_w4a16_problem* p, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* events) {
+  const int st = check_forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2,
+                               scales_w2, shared_w, out, p, workspace, workspace_bytes);
+  if (st != MOE_OK || p->num_tokens == 0) return st;
   const Layout L = layout(p);
-  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted_ids);
@@ -284,6 +296,47 @@ int moe_w4a16_forward_timed(const void* x, const int32_t* topk_ids, const float*
                             void* const* stage_events) {
   return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
                       shared_w, out, p, workspace, workspace_bytes, stream, stage_events);
+}
+
+static int check_route(const float* scores, int32_t num_scored, const moe_w4a16_problem* p,
+                       const int32_t* topk_ids, const float* topk_weights) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (num_scored < 1 || num_scored > MOE_MAX_SCORED || p->top_k > num_scored ||
+      (int64_t)p->expert_base + p->num_experts > num_scored)
+    return MOE_ERR_SHAPE;
+  if (p->num_tokens == 0) return MOE_OK;
+  if (!scores || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(topk_ids) || !aligned16(topk_weights))
+    return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+int moe_w4a16_route(const float* scores, int32_t num_scored, const moe_w4a16_problem* p,
+                    int32_t* topk_ids, float* topk_weights, void* stream) {
+  const int st = check_route(scores, num_scored, p, topk_ids, topk_weights);
+  if (st != MOE_OK || p->num_tokens == 0) return st;
+  return hip_status(moe::launch_route(scores, p->num_tokens, num_scored, p->top_k, topk_ids,
+                                      topk_weights, (hipStream_t)stream));
+}
+
+int moe_w4a16_forward_scores(const void* x, const float* scores, int32_t num_scored,
+                             const int32_t* packed_w13, const void* scales_w13,
+                             const int32_t* packed_w2, const void* scales_w2,
+                             const void* shared_w, void* out, int32_t* topk_ids,
+                             float* topk_weights, const moe_w4a16_problem* p, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  int st = check_route(scores, num_scored, p, topk_ids, topk_weights);
+  if (st != MOE_OK || p->num_tokens == 0) return st;
+  // every check of the layer call runs before the router's launch
+  st = check_forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+                     shared_w, out, p, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  st = hip_status(moe::launch_route(scores, p->num_tokens, num_scored, p->top_k, topk_ids,
+                                    topk_weights, (hipStream_t)stream));
+  if (st != MOE_OK) return st;
+  return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+                      shared_w, out, p, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* moe_w4a16_status_string(int status) {

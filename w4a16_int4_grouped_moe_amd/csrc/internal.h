@@ -64,6 +64,11 @@ int32_t prefill_block_m();  // bucket rows per block of that path
 hipError_t launch_gate_up_prefill(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream);
 
+// Router step: for each of T tokens, the k largest of S fp32 scores (equal
+// scores: lower expert first), descending, and weights = softmax over them.
+constexpr int32_t kMaxScored = 1024;  // scores per token (experts of the model)
+hipError_t launch_route(const float* scores, int64_t T, int32_t S, int32_t k, int32_t* topk_ids,
+                        float* topk_weights, hipStream_t stream);
 // out[t] = bf16(s[t] + sum_j valid * w[t,j] * y[t*k+j]), fp32 sum in slot order.
 hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
                           const float* topk_weights, uint16_t* out, int64_t T, int32_t H,
