@@ -18,7 +18,10 @@ launch stream during the timed steps), the HBM traffic measured by rocprofv3
 counters when it was taken on the current kernel source, and the fp64 CPU
 oracle timed on a bounded sample of the same workload. `per_batch` adds a
 per-stage breakdown from a short pass with all stage events after the timed
-region (`us_per_call` there includes those extra event packets).
+region (`us_per_call` there includes those extra event packets), and the time
+of the router step (scores -> top-k ids and weights) that would precede the
+layer, measured on its own (it is not part of the timed step: the layer takes
+ids and weights as inputs).
 """
 from __future__ import annotations
 
@@ -249,6 +252,24 @@ def main():
             run(c, ev)
     torch.cuda.synchronize()
 
+    # the router step in front of the layer (scores of all the model's experts
+    # -> top-k ids and weights), timed on its own per batch size: HIP events
+    # around single calls on the launch stream
+    route_us = []
+    for c in calls:
+        w = c["w"]
+        sc = torch.from_numpy(mi.router_scores(600 + w.T, w.T, g.n_experts)).to(dev)
+        rid = torch.empty((w.T, g.top_k), dtype=torch.int32, device=dev)
+        rw = torch.empty((w.T, g.top_k), dtype=torch.float32, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_diag + 1)]
+        for i in range(n_diag + 1):
+            ev[i][0].record()
+            moe.route(sc, g.top_k, num_experts=w.n_local, expert_base=w.expert_base,
+                      topk_ids=rid, topk_weights=rw)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        route_us.append(float(np.median([a.elapsed_time(b) for a, b in ev[1:]])) * 1e3)
+
     stage_names = ["align", "gate_up", "down", "combine"]
     per_batch = []
     gate_up_ms, gate_up_bytes, gate_up_flops = [], [], []
@@ -271,7 +292,8 @@ def main():
                                                        for s in range(n_diag)])) * 1e3, 2),
                        "down": round(float(np.mean([hip.elapsed_ms(diag[s][ci][2], diag[s][ci][6])
                                                     for s in range(n_diag)])) * 1e3, 2)},
-            stage_us={n: round(float(v) * 1e3, 2) for n, v in zip(stage_names, avg)}))
+            stage_us={n: round(float(v) * 1e3, 2) for n, v in zip(stage_names, avg)},
+            router_us=round(route_us[ci], 2)))
         gate_up_ms.append(float(gu.mean()))
         gate_up_bytes.append(wk["gate_up_bytes"])
         gate_up_flops.append(wk["gate_up_flops"])

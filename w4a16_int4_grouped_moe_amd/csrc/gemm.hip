@@ -38,6 +38,12 @@
 namespace moe {
 namespace {
 
+// cache policy bits of the int4 weight loads
+#ifndef MOE_TILED_AUX
+#define MOE_TILED_AUX 0
+#endif
+constexpr int kTiledAux = MOE_TILED_AUX;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -206,7 +212,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int mblk, int til
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if (INT4) {
-        bq_reg[s][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], cofs(ch, 64), 0);
+        bq_reg[s][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], cofs(ch, 64), kTiledAux);
         sc_reg[s] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[s], cofs(ch, 8), 0);
       } else {
 #pragma unroll

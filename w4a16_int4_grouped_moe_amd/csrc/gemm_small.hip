@@ -66,7 +66,14 @@ constexpr int kNRS = MOE_SMALL_NRS;  // bf16 shared-expert row-sets per wave
 constexpr int kTokBlocks = MOE_SMALL_TOKBLOCKS;
 
 // occupancy target (waves per SIMD) of a launch whose int4 waves hold NR row-sets
-constexpr int waves_per_simd(int nr) { return nr >= 8 ? 2 : 4; }
+#ifndef MOE_SMALL_WAVES
+#define MOE_SMALL_WAVES 4
+#endif
+constexpr int waves_per_simd(int nr) { return nr >= 8 ? 2 : MOE_SMALL_WAVES; }
+#ifndef MOE_SMALL_DEPTH
+#define MOE_SMALL_DEPTH 1
+#endif
+constexpr int kSmallDepth = MOE_SMALL_DEPTH;  // int4 weight iterations in flight
 constexpr int kGroupsPerIt = 16;  // k-parts = MFMA blocks
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
 constexpr uint32_t kNeg136 = 0xC308C308u;  // bf16 -136.0 in both halves
@@ -74,6 +81,20 @@ constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 constexpr int kXBytes = 4 * 64 * 16;       // activation fragments per iteration
 constexpr int kOutOfRange = (int)0x80000000u;  // buffer offset past any resource: reads 0
 constexpr int kScaleBatch = 8;             // scale pieces in flight per thread while staging
+// cache policy bits of the buffer loads: int4 weights, their scales and the
+// bf16 shared weights
+#ifndef MOE_STREAM_AUX
+#define MOE_STREAM_AUX 2  // nt: the weight stream bypasses cache retention
+#endif
+#ifndef MOE_SCALE_AUX
+#define MOE_SCALE_AUX 0
+#endif
+#ifndef MOE_SHARED_AUX
+#define MOE_SHARED_AUX 0
+#endif
+constexpr int kStreamAux = MOE_STREAM_AUX;
+constexpr int kScaleAux = MOE_SCALE_AUX;
+constexpr int kSharedAux = MOE_SHARED_AUX;
 
 // A wave-uniform byte offset for the scalar offset field of a buffer load;
 // readfirstlane makes it an SGPR value, so the compiler emits one load instead
@@ -147,7 +168,7 @@ __host__ __device__ inline int scale_row_bytes(int K) {
 
 // NB blocks of four rows starting at row0 (NB > 1 only for the bf16 shared
 // expert: its weights are then read once for 4 NB tokens).
-template <int PHASE, int NR, bool INT4, int NB>
+template <int PHASE, int NR, bool INT4, int NB, int DEPTH>
 __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, int slice0,
                                            uint8_t* lds) {
   static_assert(INT4 ? NB == 1 : NB >= 1, "int4 work items hold one block");
@@ -228,7 +249,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
           const int w = r / (4 * NR), lr = r % (4 * NR);
           off = (weight_row<PHASE, NR>(p, slice0 + w, lr / 4, lr % 4) * (K / 32) + pc * 8) * 2;
         }
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, 0);
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, kScaleAux);
       }
 #pragma unroll
       for (int u = 0; u < kScaleBatch; ++u) {
@@ -289,12 +310,13 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) {
       if (INT4) {
-        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], kofs(it, kGroupsPerIt * 16), 0);
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], kofs(it, kGroupsPerIt * 16),
+                                                           kStreamAux);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           f.w[rs][q] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs] + 16 * q,
-                                                             kofs(it, kGroupsPerIt * 64), 0);
+                                                             kofs(it, kGroupsPerIt * 64), kSharedAux);
       }
     }
     // Groups past the end of K (a partial last iteration) need no masking:
@@ -393,33 +415,36 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
     }
   };
 
-  // ---- pipeline: stage it+1 loads in flight while stage it is computed ------
-  uint8_t* st0 = lds;
-  uint8_t* st1 = lds + stage_bytes<NB>();
-  Frag fa, fb;
+  // ---- pipeline: the weights of DEPTH iterations and the activations of the
+  // next one are in flight while an iteration is computed (a ring of DEPTH + 1
+  // weight stages, two activation stages in LDS) --------------------------------
+  uint8_t* const st[2] = {lds, lds + stage_bytes<NB>()};
+  Frag f[DEPTH + 1];
   load_shared(0);
-  load_w(fa, 0);
-  // the scales are fetched together with the first iteration's operands
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    load_w(f[d], d);
+    __builtin_amdgcn_sched_barrier(0);  // keep the iterations' loads in issue order
+  }
+  // the scales are fetched together with the first iterations' operands
   if (INT4) stage_scales();
-  store_shared(st0, 0);
+  store_shared(st[0], 0);
   __syncthreads();
   // (the scheduling barriers keep the prefetch ahead of the computation: left
   // free, the scheduler sinks the loads below it to save registers)
-  for (int it = 0; it < niters; it += 2) {
-    load_shared(it + 1);
-    load_w(fb, it + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(fa, st0, it);
-    if (it + 1 >= niters) break;
-    store_shared(st1, it + 1);
-    __syncthreads();
-    load_shared(it + 2);
-    load_w(fa, it + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(fb, st1, it + 1);
-    if (it + 2 >= niters) break;
-    store_shared(st0, it + 2);
-    __syncthreads();
+  constexpr int kPeriod = (DEPTH + 1) % 2 ? 2 * (DEPTH + 1) : DEPTH + 1;
+  for (int it0 = 0; it0 < niters; it0 += kPeriod) {
+#pragma unroll
+    for (int u = 0; u < kPeriod; ++u) {
+      const int it = it0 + u;
+      load_shared(it + 1);
+      load_w(f[(u + DEPTH) % (DEPTH + 1)], it + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f[u % (DEPTH + 1)], st[u % 2], it);
+      if (it + 1 >= niters) break;
+      store_shared(st[(u + 1) % 2], it + 1);
+      __syncthreads();
+    }
   }
 
   // ---- per block: sum the k-parts (every lane then holds all NR x 4 results
@@ -501,14 +526,14 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kerne
   if (bid < shared) {
     const int64_t tg = bid / ns;
     const int s = (int)(bid - tg * ns);
-    small_tile<PHASE, NRS, false, kTokBlocks>(p, tg * 4 * kTokBlocks, s * kWaves, lds);
+    small_tile<PHASE, NRS, false, kTokBlocks, 1>(p, tg * 4 * kTokBlocks, s * kWaves, lds);
   } else {
     const int wg_slices = p.N / slice_cols<PHASE, NR>() / kWaves;
     const int64_t b2 = bid - shared;
     const int64_t blk = b2 / wg_slices;
     const int s = (int)(b2 - blk * wg_slices);
     if (blk * 4 >= *p.n_padded) return;
-    small_tile<PHASE, NR, true, 1>(p, blk * 4, s * kWaves, lds);
+    small_tile<PHASE, NR, true, 1, kSmallDepth>(p, blk * 4, s * kWaves, lds);
   }
 }
 
@@ -622,13 +647,14 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) {
       if (INT4) {
-        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], sofs(step, wstep), 0);
-        f.s[rs] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rs], sofs(step, sstep), 0);
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], sofs(step, wstep),
+                                                           kStreamAux);
+        f.s[rs] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rs], sofs(step, sstep), kScaleAux);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           f.w[rs][q] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs] + 16 * q,
-                                                             sofs(step, wstep), 0);
+                                                             sofs(step, wstep), kSharedAux);
       }
     }
   };
