@@ -22,9 +22,14 @@
  *    "host". Every device pointer must be 16-byte aligned.
  *  - The caller allocates and owns every buffer, including the workspace, and
  *    keeps it alive until the stream work completes. The library allocates
- *    nothing, keeps no pointer after it returns, never synchronises the host
- *    and launches only on `stream` (a hipStream_t; NULL is the null stream) on
- *    the current device. Calls that share a workspace must not overlap.
+ *    no buffers, keeps no pointer after it returns, never synchronises the
+ *    host and launches only on `stream` (a hipStream_t; NULL is the null
+ *    stream) on the current device. Calls that share a workspace must not
+ *    overlap. One exception to "no allocation": prefill-sized calls (see
+ *    moe_w4a16_forward_block_m: 96) run the bf16 shared expert's two dense
+ *    GEMMs in hipBLASLt, whose handle is created on the first such call on a
+ *    device and kept until the process ends (its plans are cached per shape);
+ *    make one such call before capturing them into a HIP graph.
  *  - Every argument error is detected on the host before any launch (so a
  *    failing call writes nothing) and reported as a negative status. Routing
  *    data on the device is never an error: ids outside [expert_base,

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 H, I, E, K = 512, 256, 16, 4
 
 
-@pytest.fixture(scope="module", params=[96, 8], ids=["tiled", "small-batch"])
+@pytest.fixture(scope="module", params=[96, 8, 300], ids=["tiled", "small-batch", "prefill"])
 def setup(request):
     import torch
 

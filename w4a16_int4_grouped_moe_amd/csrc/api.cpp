@@ -54,7 +54,7 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
 constexpr int64_t kAlignMultiMin = 8192;
 
 struct Layout {
-  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, total;
+  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, shared_gu, blas, total;
   int64_t cap_rows;
   int32_t max_blocks, bm;
 };
@@ -77,6 +77,14 @@ Layout layout(const moe_w4a16_problem* p) {
   L.align_scratch = o;
   if ((int64_t)P >= kAlignMultiMin)
     o = round_up(o + 4 * (size_t)moe::align_scratch_ints((int64_t)P, p->num_experts));
+  // prefill-sized blocks: the shared expert's gate/up output (fp32) and the
+  // library GEMM's workspace
+  L.shared_gu = L.blas = o;
+  if (L.bm == moe::prefill_block_m()) {
+    o = round_up(o + 4 * T * 2 * I);
+    L.blas = o;
+    o = round_up(o + moe::kSharedBlasWorkspace);
+  }
   L.total = o;
   return L;
 }
@@ -228,6 +236,19 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
     e = gate_up ? moe::launch_gate_up_prefill(gp, strm) : moe::launch_down_prefill(gp, strm);
     if (e == hipSuccess) e = mark(after_routed);
     if (e != hipSuccess || !gp.wshared) return e;
+    // the bf16 shared expert: dense GEMMs in hipBLASLt, SwiGLU in our kernel;
+    // where the library finds no algorithm, the tiled kernel below
+    if (gate_up) {
+      float* gu = reinterpret_cast<float*>(ws + L.shared_gu);
+      e = moe::launch_shared_blas(gp.wshared, gp.a_shared, gu, 2 * (int64_t)I, T, H, ws + L.blas,
+                                  strm);
+      if (e == hipSuccess) return moe::launch_swiglu(gu, gp.h_shared, T, I, strm);
+    } else {
+      e = moe::launch_shared_blas(gp.wshared, gp.a_shared, gp.y_shared, H, T, I, ws + L.blas,
+                                  strm);
+      if (e == hipSuccess) return e;
+    }
+    if (e != hipErrorNotSupported) return e;
     moe::GemmParams gs = gp;
     gs.max_blocks = 0;  // shared-expert tiles only
     return gate_up ? moe::launch_gate_up(gs, 64, strm) : moe::launch_down(gs, 64, strm);

@@ -69,6 +69,16 @@ hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream);
 constexpr int32_t kMaxScored = 1024;  // scores per token (experts of the model)
 hipError_t launch_route(const float* scores, int64_t T, int32_t S, int32_t k, int32_t* topk_ids,
                         float* topk_weights, hipStream_t stream);
+// Dense bf16 GEMM of the shared expert (hipBLASLt; see shared_blas.cpp):
+// out [T, rows] fp32 = act [T, K] . weights [rows, K]^T, with
+// kSharedBlasWorkspace bytes of library workspace. hipErrorNotSupported when
+// the library offers no algorithm for the shape (nothing was launched).
+constexpr size_t kSharedBlasWorkspace = size_t(32) << 20;
+hipError_t launch_shared_blas(const uint16_t* weights, const uint16_t* act, float* out,
+                              int64_t rows, int64_t T, int64_t K, void* workspace,
+                              hipStream_t stream);
+// h [T, I] bf16 = silu(gu[:, :I]) * gu[:, I:] from fp32 gu [T, 2I].
+hipError_t launch_swiglu(const float* gu, uint16_t* h, int64_t T, int32_t I, hipStream_t stream);
 // out[t] = bf16(s[t] + sum_j valid * w[t,j] * y[t*k+j]), fp32 sum in slot order.
 hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
                           const float* topk_weights, uint16_t* out, int64_t T, int32_t H,
