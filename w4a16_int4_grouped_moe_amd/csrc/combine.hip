@@ -32,6 +32,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kBufferFlags = 0x00020000;       // raw buffer resource, dword 3
 constexpr int kOutOfRange = (int)0x80000000u;  // buffer offset past any resource: reads 0
 constexpr int kSlotBatch = 8;                  // slots whose loads are in flight together
+#ifndef MOE_Y_AUX
+#define MOE_Y_AUX 2
+#endif
+constexpr int kYAux = MOE_Y_AUX;  // cache policy of the y loads (read once)
 
 // The loads of slots j0 .. j0 + kSlotBatch - 1 (all of them inside k when
 // FULL: their ids and weights are then read with unconditional scalar loads)
@@ -55,7 +59,8 @@ __device__ __forceinline__ void combine_slots(f32x4& acc, __amdgpu_buffer_rsrc_t
 #pragma unroll
   for (int u = 0; u < kSlotBatch; ++u)
     v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         yres, ok[u] ? ((j0 + u) * H + n) * 4 : kOutOfRange, 0, 0));
+                                         yres, ok[u] ? ((j0 + u) * H + n) * 4 : kOutOfRange, 0,
+                                         kYAux));
 #pragma unroll
   for (int u = 0; u < kSlotBatch; ++u) {
     if (!ok[u]) continue;

@@ -103,24 +103,38 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
 }
 
+// Per-group dequantisation constants: the scale s, -1032 s, s / 16 and -72 s.
+struct GroupScale {
+  float s, c1032, s16, c72;
+};
+__device__ __forceinline__ GroupScale group_scale(float s) {
+  return GroupScale{s, -1032.0f * s, 0.0625f * s, -72.0f * s};
+}
+
 // The eight codes of one word -> eight bf16 weights (u - 8) * s in input order.
-// Fields k and k + 4 are OR-ed into the fp16 pattern 0x6400, which is exactly
-// the fp16 value 1024 + u (one shift and one v_bitop3 per pair); one mixed
-// fp16/fp32 FMA per code, fma(1024 + u, s, -1032 s), gives (u - 8) * s exactly
-// in fp32 (the product has at most 19 significant bits and so has 1032 s), and
-// it is rounded once to bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float c1032) {
-  f32x2 v[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const h16x2 h = __builtin_bit_cast(h16x2, and_or(w >> (4 * k), 0x000F000Fu, 0x64006400u));
-    v[k] = f32x2{fmaf((float)h[0], s, c1032), fmaf((float)h[1], s, c1032)};  // u_k, u_{k+4}
-  }
+// A field in bits 0-3 of a 16-bit half OR-ed into the fp16 pattern 0x6400 is
+// exactly the fp16 value 1024 + u, a field in bits 4-7 gives 1024 + 16 u, so
+// the word's low byte pair (fields 0, 4 and 1, 5) needs no shift and its high
+// byte pair (fields 2, 6 and 3, 7) one shift by 8: one shift and four
+// v_bitop3 per word. One mixed fp16/fp32 FMA per code, fma(1024 + u, s,
+// -1032 s) or fma(1024 + 16 u, s / 16, -72 s), gives (u - 8) * s exactly in
+// fp32 (the products have at most 19 significant bits, and s / 16, 1032 s and
+// 72 s are exact), which is rounded once to bf16.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, const GroupScale& g) {
+  const uint32_t w8 = w >> 8;
+  const h16x2 h0 = __builtin_bit_cast(h16x2, and_or(w, 0x000F000Fu, 0x64006400u));   // u0, u4
+  const h16x2 h1 = __builtin_bit_cast(h16x2, and_or(w, 0x00F000F0u, 0x64006400u));   // u1, u5
+  const h16x2 h2 = __builtin_bit_cast(h16x2, and_or(w8, 0x000F000Fu, 0x64006400u));  // u2, u6
+  const h16x2 h3 = __builtin_bit_cast(h16x2, and_or(w8, 0x00F000F0u, 0x64006400u));  // u3, u7
+  const f32x2 v0 = {fmaf((float)h0[0], g.s, g.c1032), fmaf((float)h0[1], g.s, g.c1032)};
+  const f32x2 v1 = {fmaf((float)h1[0], g.s16, g.c72), fmaf((float)h1[1], g.s16, g.c72)};
+  const f32x2 v2 = {fmaf((float)h2[0], g.s, g.c1032), fmaf((float)h2[1], g.s, g.c1032)};
+  const f32x2 v3 = {fmaf((float)h3[0], g.s16, g.c72), fmaf((float)h3[1], g.s16, g.c72)};
   u32x4 r;
-  r[0] = pack_bf16x2(v[0][0], v[1][0]);
-  r[1] = pack_bf16x2(v[2][0], v[3][0]);
-  r[2] = pack_bf16x2(v[0][1], v[1][1]);
-  r[3] = pack_bf16x2(v[2][1], v[3][1]);
+  r[0] = pack_bf16x2(v0[0], v1[0]);
+  r[1] = pack_bf16x2(v2[0], v3[0]);
+  r[2] = pack_bf16x2(v0[1], v1[1]);
+  r[3] = pack_bf16x2(v2[1], v3[1]);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -260,12 +274,12 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const float (&sc)[kNSub]) {
-    float c1032[kNSub];
+    GroupScale gs[kNSub];
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) c1032[s] = -1032.0f * sc[s];
+    for (int s = 0; s < kNSub; ++s) gs[s] = group_scale(sc[s]);
     bf16x8 bw[2][kNSub];  // this step's and the next step's weights
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) bw[0][s] = dequant8(w[s][0], sc[s], c1032[s]);
+    for (int s = 0; s < kNSub; ++s) bw[0][s] = dequant8(w[s][0], gs[s]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8 a[MS];
@@ -276,7 +290,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       if (j < 3) {
 #pragma unroll
         for (int s = 0; s < kNSub; ++s)
-          bw[(j + 1) & 1][s] = dequant8(w[s][j + 1], sc[s], c1032[s]);
+          bw[(j + 1) & 1][s] = dequant8(w[s][j + 1], gs[s]);
       }
 #pragma unroll
       for (int mi = 0; mi < MS; ++mi)
