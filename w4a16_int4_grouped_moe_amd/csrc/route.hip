@@ -7,13 +7,14 @@
 // is taken (softmax over all experts renormalised over the k selected equals
 // the softmax over the selected scores).
 //
-// One wave per token, four tokens per work-group. Each score becomes a 64-bit
-// key, (order-preserving image of the float) << 32 | ~expert, so one unsigned
-// maximum picks the largest score and, among equal scores, the lowest expert
-// (-0.0 is mapped to +0.0 first). k rounds of a wave-wide maximum select the
-// experts; the owner lane retires the winner's key. Lane j keeps round j's
-// score, and lanes j < k then form the softmax in fp32 (expf, IEEE division),
-// summed by a fixed butterfly, so the result does not depend on timing.
+// One wave per token, four tokens per work-group. Each score becomes a 32-bit
+// key, an order-preserving image of the float (-0.0 mapped to +0.0 first), so
+// that an unsigned maximum picks the largest score. Each of k rounds takes the
+// wave-wide maximum key (DPP row shifts and row broadcasts, no LDS), then the
+// lowest expert holding it (a ballot per register, lowest register first:
+// expert = lane + 64 * register), and the owner lane retires that key. Lane j
+// keeps round j's score, and lanes j < k then form the softmax in fp32
+// (expf, IEEE division) with a fixed DPP summation order.
 #include "internal.h"
 
 namespace moe {
@@ -34,19 +35,25 @@ __device__ __forceinline__ float key_value(uint32_t key) {
   return __builtin_bit_cast(float, u);
 }
 
-__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t o = __shfl_xor(v, d);
-    v = o > v ? o : v;
-  }
-  return v;
+// x moved across lanes by a DPP control; lanes without a source, or outside
+// ROW_MASK, read 0 (the identity of both reductions below)
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp(T x) {
+  const int i = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, i, CTRL, ROW_MASK, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d);
-  return v;
+// op (an unsigned max or a float sum) over the wave in a fixed order,
+// returned to every lane
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp<0x111, 0xF>(v));  // row_shr:1
+  v = op(v, dpp<0x112, 0xF>(v));  // row_shr:2
+  v = op(v, dpp<0x114, 0xF>(v));  // row_shr:4
+  v = op(v, dpp<0x118, 0xF>(v));  // row_shr:8: lane 15 of each row holds the row
+  v = op(v, dpp<0x142, 0xA>(v));  // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp<0x143, 0xC>(v));  // row_bcast:31 into rows 2 and 3: lane 63 holds all
+  return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ scores,
@@ -67,23 +74,28 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
     key[i] = e < S ? order_key(row[e]) : 0u;
   }
 
+  auto umax = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
   uint32_t mine = 0;  // lane j: the key of round j
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < kPerLane; ++i) best = umax(best, key[i]);
+    const uint32_t m = wave_reduce(best, umax);
+    int e = 0;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
-      const uint64_t c =
-          key[i] ? ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(lane + 64 * i) : 0ull;
-      best = c > best ? c : best;
+      const uint64_t b = __ballot(key[i] == m);
+      if (b) {
+        e = 64 * i + __builtin_ctzll(b);
+        break;
+      }
     }
-    best = wave_max(best);
-    const int e = (int)~(uint32_t)best;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i)
       if (lane + 64 * i == e) key[i] = 0u;
     if (lane == j) {
-      mine = (uint32_t)(best >> 32);
+      mine = m;
       my_id = e;
     }
   }
@@ -91,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
   // softmax over the k selected scores; round 0 holds the largest
   const float top = key_value(__builtin_amdgcn_readfirstlane(mine));
   const float z = lane < k ? expf(key_value(mine) - top) : 0.f;
-  const float sum = wave_sum(z);
+  const float sum = wave_reduce(z, [](float a, float b) { return a + b; });
   if (lane < k) {
     topk_ids[t * k + lane] = my_id;
     topk_weights[t * k + lane] = z / sum;
