@@ -64,6 +64,10 @@ constexpr int kNRDown = MOE_SMALL_NR_DOWN;   // down
 #endif
 constexpr int kNRS = MOE_SMALL_NRS;  // bf16 shared-expert row-sets per wave
 constexpr int kTokBlocks = MOE_SMALL_TOKBLOCKS;
+#ifndef MOE_SMALL_TOKBLOCKS_LARGE
+#define MOE_SMALL_TOKBLOCKS_LARGE 4
+#endif
+constexpr int kTokBlocksLarge = MOE_SMALL_TOKBLOCKS_LARGE;  // for batches beyond 4 kTokBlocks
 
 // occupancy target (waves per SIMD) of a launch whose int4 waves hold NR row-sets
 #ifndef MOE_SMALL_WAVES
@@ -512,21 +516,21 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 // One work-group = one block of rows x 4 consecutive wave slices, numbered
 // block-major (consecutive work-groups stream consecutive rows of one expert;
 // the default round-robin placement then spreads them over the XCDs). The
-// shared expert's work-groups (kTokBlocks 4-token blocks each) come first:
-// each streams twice the bytes of a routed one (bf16 weights), so starting
-// them first keeps them out of the kernel's tail. Routed work-groups (one
-// 4-row bucket block each) follow.
-template <int PHASE, int NR, int NRS>
+// shared expert's work-groups (TB 4-token blocks each: every such group of
+// tokens reads the shared weights once) come first: each streams twice the
+// bytes of a routed one (bf16 weights), so starting them first keeps them out
+// of the kernel's tail. Routed work-groups (one 4-row bucket block each)
+// follow.
+template <int PHASE, int NR, int NRS, int TB>
 __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // small_lds_bytes
   const int64_t bid = blockIdx.x;
   const int ns = p.N / slice_cols<PHASE, NRS>() / kWaves;
-  const int64_t shared =
-      p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) * ns : 0;
+  const int64_t shared = p.wshared ? (p.T + 4 * TB - 1) / (4 * TB) * ns : 0;
   if (bid < shared) {
     const int64_t tg = bid / ns;
     const int s = (int)(bid - tg * ns);
-    small_tile<PHASE, NRS, false, kTokBlocks, 1>(p, tg * 4 * kTokBlocks, s * kWaves, lds);
+    small_tile<PHASE, NRS, false, TB, 1>(p, tg * 4 * TB, s * kWaves, lds);
   } else {
     const int wg_slices = p.N / slice_cols<PHASE, NR>() / kWaves;
     const int64_t b2 = bid - shared;
@@ -832,23 +836,23 @@ hipError_t launch_narrow(const GemmParams& p, hipStream_t stream) {
 
 // Dynamic LDS of a launch: two activation stages (of the larger of the routed
 // and the shared work items) and, for the routed ones, the staged scales.
-template <int NR>
+template <int NR, int TB = kTokBlocksLarge>
 int small_lds_bytes(int K) {
   const int routed = 2 * stage_bytes<1>() + kWaves * 4 * NR * scale_row_bytes(K);
-  const int shared = 2 * stage_bytes<kTokBlocks>();
+  const int shared = 2 * stage_bytes<TB>();
   return routed > shared ? routed : shared;
 }
 constexpr int kMaxLds = 64 * 1024;
 
-template <int PHASE, int NR, int NRS>
-hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
+template <int PHASE, int NR, int NRS, int TB>
+hipError_t launch_small_tb(const GemmParams& p, hipStream_t stream) {
   // every work-group holds whole 4-slice groups: N must split evenly
   if (p.N % (slice_cols<PHASE, NR>() * kWaves) || p.N % (slice_cols<PHASE, NRS>() * kWaves))
     return hipErrorInvalidValue;
-  const int lds = small_lds_bytes<NR>(p.K);
+  const int lds = small_lds_bytes<NR, TB>(p.K);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int64_t routed = (int64_t)p.max_blocks * (p.N / slice_cols<PHASE, NR>() / kWaves);
-  const int64_t shared = p.wshared ? (p.T + 4 * kTokBlocks - 1) / (4 * kTokBlocks) *
+  const int64_t shared = p.wshared ? (p.T + 4 * TB - 1) / (4 * TB) *
                                          (p.N / slice_cols<PHASE, NRS>() / kWaves)
                                    : 0;
   const int64_t grid = routed + shared;
@@ -856,8 +860,17 @@ hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS, TB>),
                          dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
+}
+
+// A few tokens: the shared weights are read once per 4 kTokBlocks tokens by
+// many small work-groups; more tokens: once per 4 kTokBlocksLarge tokens,
+// fewer re-reads of the shared weights for the same per-weight arithmetic.
+template <int PHASE, int NR, int NRS>
+hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
+  if (p.T > 4 * kTokBlocks) return launch_small_tb<PHASE, NR, NRS, kTokBlocksLarge>(p, stream);
+  return launch_small_tb<PHASE, NR, NRS, kTokBlocks>(p, stream);
 }
 
 }  // namespace
