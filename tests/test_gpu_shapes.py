@@ -1,0 +1,64 @@
+"""Layer parity over a spread of shapes that reach every kernel path and its
+edges: K not a multiple of the small-batch iteration (partial last
+iteration), down widths that take the narrow-K kernel (I = 128, 384), the
+largest top-k (16) and expert count (512), expert bases with non-local ids,
+ragged token counts, and each block size (4, 16, 64, 96).
+
+The 16-, 64- and 96-row paths round each dequantised weight to bf16 before its
+product (the small-batch path keeps it exact), which about doubles the
+output's error: with no shared expert and a few hundred thousand outputs its
+largest elementwise error reaches about 2e-2 rms(ref) (a ~6-sigma tail), so
+the prefill case without a shared expert is sized at 160 tokens."""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+from tests.helpers import check, run_layer
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # T, H, I, E, k, base, shared, expected block_m
+    (3, 640, 384, 8, 2, 0, True, 4),       # K = 640: one full and one partial iteration
+    (5, 1152, 640, 6, 3, 1, False, 4),     # K = 1152 and a down K of 640 (partial iterations)
+    (1, 384, 128, 16, 16, 0, True, 4),     # top-16, narrow down (I = 128)
+    (8, 256, 128, 512, 8, 0, True, 4),     # 512 local experts
+    (33, 640, 384, 8, 4, 0, True, 16),     # 16-row blocks, ragged T
+    (97, 384, 640, 6, 2, 2, True, 64),     # 64-row blocks, expert base
+    (700, 1536, 512, 10, 2, 0, True, 96),  # prefill blocks, shared expert in the library GEMM
+    (160, 1024, 768, 4, 3, 0, False, 96),  # prefill blocks, no shared expert, I = 768
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("T,H,I,E,k,base,shared,bm", CASES)
+def test_shape(dev, T, H, I, E, k, base, shared, bm):
+    import torch
+    import w4a16_int4_grouped_moe_amd as moe
+
+    got_bm = moe.forward_block_m(moe.problem(T, H, I, E, k, base))
+    assert got_bm == bm, got_bm
+    seed = 1000 + T + H + I
+    n_global = base + E + 2
+    bank = mi.weight_bank(seed, H, I, list(range(base, base + E)))
+    bank_dev = {kk: mi.to_device(v, dev) for kk, v in bank.__dict__.items()}
+    x = mi.activations(seed + 1, T, H)
+    ids, w = mi.routing_uniform(seed + 2, T, n_global, min(k, n_global))
+    if base:
+        ids[::5, 0] = -1
+    sw = mi.shared_weights(seed + 3, H, I) if shared else None
+    print(f"[case] T={T} H={H} I={I} E={E} k={k} base={base} shared={shared} bm={bm}",
+          flush=True)
+    out = run_layer(dev, x, ids, w, bank_dev, sw, expert_base=base)
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw, base)
+    check(mi.bf16_tensor_to_f64(out), ref, f"T={T} H={H} I={I} E={E} k={k} bm={bm}")

@@ -577,14 +577,18 @@ template <int KG, int NR>
 constexpr int narrow_rows() { return 4 * NR * (16 / KG); }
 
 // NB blocks of four rows (routed: one 4-row bucket block; shared: NB blocks of
-// consecutive tokens) against weight rows [n0, n0 + nsteps * kWaves * RW).
+// consecutive tokens) against the weight rows of kNarrowSteps wave steps from
+// n0 (fewer where N ends first: a wave takes the steps that start below N).
 template <int KG, int NR, bool INT4, int NB, int DEPTH>
-__device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, int n0,
-                                            int nsteps) {
+__device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, int n0) {
   constexpr int RC = 16 / KG;
   constexpr int RW = narrow_rows<KG, NR>();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  // steps of this wave: those whose RW rows start below N (N is a multiple of RW)
+  const int avail = p.N - n0 - wave * RW;
+  const int nsteps =
+      uniform(avail <= 0 ? 0 : min(kNarrowSteps, (avail + kWaves * RW - 1) / (kWaves * RW)));
   const int kp = lane >> 2;
   const int j = lane & 3;
   const int c = kp / KG;
@@ -792,16 +796,14 @@ __global__ __launch_bounds__(kThreads, MOE_NARROW_WAVES) void narrow_down_kernel
   if (bid < shared) {
     const int64_t tg = bid / cs;
     const int n0 = (int)(bid - tg * cs) * kRowsWGs;
-    const int nsteps = min(kNarrowSteps, (p.N - n0) / (kWaves * narrow_rows<KG, NRS>()));
-    narrow_tile<KG, NRS, false, kTokBlocks, 1>(p, tg * 4 * kTokBlocks, n0, nsteps);
+    narrow_tile<KG, NRS, false, kTokBlocks, 1>(p, tg * 4 * kTokBlocks, n0);
   } else {
     const int cr = (p.N + kRowsWG - 1) / kRowsWG;
     const int64_t b2 = bid - shared;
     const int64_t blk = b2 / cr;
     const int n0 = (int)(b2 - blk * cr) * kRowsWG;
     if (blk * 4 >= *p.n_padded) return;
-    const int nsteps = min(kNarrowSteps, (p.N - n0) / (kWaves * narrow_rows<KG, NR>()));
-    narrow_tile<KG, NR, true, 1, kNarrowDepth>(p, blk * 4, n0, nsteps);
+    narrow_tile<KG, NR, true, 1, kNarrowDepth>(p, blk * 4, n0);
   }
 }
 
@@ -815,9 +817,8 @@ __global__ __launch_bounds__(kThreads, MOE_NARROW_WAVES) void narrow_down_kernel
 template <int KG>
 hipError_t launch_narrow(const GemmParams& p, hipStream_t stream) {
   constexpr int NR = MOE_NARROW_NR, NRS = MOE_NARROW_NRS;
-  // whole wave steps only
-  if (p.N % (kWaves * narrow_rows<KG, NR>()) || p.N % (kWaves * narrow_rows<KG, NRS>()) ||
-      p.K > 512 || p.K % 32)
+  // whole wave steps only (a work-group's last step may hold fewer waves)
+  if (p.N % narrow_rows<KG, NR>() || p.N % narrow_rows<KG, NRS>() || p.K > 512 || p.K % 32)
     return hipErrorInvalidValue;
   constexpr int kRowsWGs = kNarrowSteps * kWaves * narrow_rows<KG, NRS>();
   constexpr int kRowsWG = kNarrowSteps * kWaves * narrow_rows<KG, NR>();
