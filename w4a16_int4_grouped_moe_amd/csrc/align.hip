@@ -7,38 +7,60 @@
 // (Changes list) need such a bucketing; the pages leave its form open, and this
 // ordering (ascending p inside a bucket) is the one the library fixes.
 //
-// Small P: one work-group of 16 waves does everything in a single launch:
+// Small P: one work-group of 8 waves does everything in a single launch:
 //   1. each wave histograms a contiguous chunk of pairs (LDS atomics; counts
 //      do not depend on order);
 //   2. per expert: prefix of the wave counts, padded size, block-wide scan of
 //      the padded sizes -> bucket offsets and n_padded;
-//   3. each wave walks its chunk 64 pairs at a time in pair order; equal
-//      experts inside the 64 are ranked by lane with ballots, so positions are
-//      exactly the stable order (no order-dependent atomics);
+//   3. each wave walks its chunk 64 pairs at a time in pair order; the lanes
+//      of a step that share an expert are ranked by lane: each lane ORs its
+//      bit into the expert's 64-bit lane mask in a per-wave LDS table (an OR
+//      does not depend on order), reads the mask back and counts the lower
+//      lanes, so positions are exactly the stable order;
 //   4. sentinel padding and block_expert.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;  // at least MOE_MAX_EXPERTS: thread e owns expert e in the scans
 constexpr int kWaves = kThreads / 64;
+
+// The lanes of this wave that hold expert e (e < 0: none), as a lane mask:
+// each lane ORs its bit into the expert's entry of the wave's own LDS table (an
+// OR does not depend on order) and reads the entry back (a wave's LDS
+// operations complete in issue order). The caller's lowest lane of the group
+// clears the entry before the table is used again.
+__device__ __forceinline__ uint64_t lane_group(uint64_t* wmask, int e, int lane) {
+  if (e < 0) return 0;
+  __hip_atomic_fetch_or(&wmask[e], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __hip_atomic_load(&wmask[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void clear_lane_group(uint64_t* wmask, int e) {
+  __hip_atomic_store(&wmask[e], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t P, int E, int base, int bm,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ n_padded_out) {
   extern __shared__ int32_t smem[];
-  volatile int32_t* hist = smem;             // [kWaves][E]: counts, then write cursors
+  int32_t* hist = smem;                      // [kWaves][E]: counts, then write cursors
   int32_t* off = smem + kWaves * E;          // [E] bucket start
   int32_t* cnt = off + E;                    // [E] valid pairs per expert
   int32_t* wsum = cnt + E;                   // [kWaves] scan partials
+  // [kWaves][E] lane masks; the offset, 4 (18 E + 16) bytes, is a multiple of 8
+  uint64_t* masks = reinterpret_cast<uint64_t*>(smem + kWaves * E + 2 * E + kWaves);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < kWaves * E; i += kThreads) {
+    hist[i] = 0;
+    masks[i] = 0;
+  }
   __syncthreads();
 
   // contiguous chunk of this wave, a multiple of 64 pairs long
@@ -49,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   // 1. histogram
   for (int64_t p = c0 + lane; p < c1; p += 64) {
     const int e = ids[p] - base;
-    if ((unsigned)e < (unsigned)E) atomicAdd((int32_t*)&hist[wave * E + e], 1);
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave * E + e], 1);
   }
   __syncthreads();
 
@@ -91,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   __syncthreads();
 
   // 3. stable scatter, 64 pairs at a time in pair order
+  uint64_t* const wmask = masks + wave * E;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t p0 = c0; p0 < c1; p0 += 64) {
     const int64_t p = p0 + lane;
@@ -99,22 +122,16 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
       const int t = ids[p] - base;
       if ((unsigned)t < (unsigned)E) e = t;
     }
-    uint64_t active = __ballot(e >= 0);
-    int rank = 0, group = 0;
-    while (active) {
-      const int leader = __builtin_ctzll(active);
-      const int key = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t m = __ballot(e == key);
-      if (e == key) {
-        rank = __popcll(m & lt_mask);
-        group = __popcll(m);
-      }
-      active &= ~m;
-    }
+    const uint64_t m = lane_group(wmask, e, lane);
+    const int rank = __popcll(m & lt_mask);
+    const int group = __popcll(m);
     if (e >= 0) {
       const int cursor = hist[wave * E + e];
       sorted_ids[cursor + rank] = (int32_t)p;
-      if (rank == 0) hist[wave * E + e] = cursor + group;
+      if (rank == 0) {
+        hist[wave * E + e] = cursor + group;
+        clear_lane_group(wmask, e);
+      }
     }
   }
   __syncthreads();
@@ -215,15 +232,19 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
 __global__ __launch_bounds__(kMultiThreads) void align_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t P, int E, int base,
     const int32_t* __restrict__ cursors, int32_t* __restrict__ sorted_ids) {
-  extern __shared__ int32_t cur_lds[];  // [kMultiWaves][E]
-  volatile int32_t* cur = cur_lds;
+  extern __shared__ int32_t cur_lds[];  // [kMultiWaves][E] cursors, then lane masks
+  int32_t* cur = cur_lds;
+  // [kMultiWaves][E] lane masks; the offset, 16 E bytes, is a multiple of 8
+  uint64_t* masks = reinterpret_cast<uint64_t*>(cur_lds + kMultiWaves * E);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nq = (P + kChunk - 1) / kChunk;
   for (int i = tid; i < kMultiWaves * E; i += kMultiThreads) {
     const int64_t qq = (int64_t)blockIdx.x * kMultiWaves + i / E;
     cur[i] = qq < nq ? cursors[qq * E + i % E] : 0;
+    masks[i] = 0;
   }
   __syncthreads();
+  uint64_t* const wmask = masks + wave * E;
   const int64_t q = (int64_t)blockIdx.x * kMultiWaves + wave;
   const int64_t c0 = q * kChunk;
   const int64_t c1 = c0 + kChunk < P ? c0 + kChunk : P;
@@ -235,22 +256,16 @@ __global__ __launch_bounds__(kMultiThreads) void align_scatter_kernel(
       const int t = ids[p] - base;
       if ((unsigned)t < (unsigned)E) e = t;
     }
-    uint64_t active = __ballot(e >= 0);
-    int rank = 0, group = 0;
-    while (active) {
-      const int leader = __builtin_ctzll(active);
-      const int key = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t m = __ballot(e == key);
-      if (e == key) {
-        rank = __popcll(m & lt_mask);
-        group = __popcll(m);
-      }
-      active &= ~m;
-    }
+    const uint64_t m = lane_group(wmask, e, lane);
+    const int rank = __popcll(m & lt_mask);
+    const int group = __popcll(m);
     if (e >= 0) {
       const int cursor = cur[wave * E + e];
       sorted_ids[cursor + rank] = (int32_t)p;
-      if (rank == 0) cur[wave * E + e] = cursor + group;
+      if (rank == 0) {
+        cur[wave * E + e] = cursor + group;
+        clear_lane_group(wmask, e);
+      }
     }
   }
 }
@@ -274,7 +289,8 @@ hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int
                      stream, topk_ids, P, E, base, scratch);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), 0, stream, P, E, block_m, scratch,
                      sorted_ids, block_expert, n_padded);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)groups), dim3(kMultiThreads), lds,
+  hipLaunchKernelGGL(align_scatter_kernel, dim3((unsigned)groups), dim3(kMultiThreads),
+                     lds + sizeof(uint64_t) * (size_t)kMultiWaves * E,
                      stream, topk_ids, P, E, base, scratch, sorted_ids);
   return hipGetLastError();
 }
@@ -282,7 +298,8 @@ hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* n_padded, hipStream_t stream) {
-  const size_t lds = sizeof(int32_t) * (size_t)(kWaves * E + 2 * E + kWaves);
+  const size_t lds =
+      sizeof(int32_t) * (size_t)(kWaves * E + 2 * E + kWaves) + sizeof(uint64_t) * kWaves * E;
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), lds, stream, topk_ids, P, E, base,
                      block_m, sorted_ids, block_expert, n_padded);
   return hipGetLastError();

@@ -8,7 +8,7 @@
 namespace moe {
 
 // Bucketing: stable counting sort of valid (token, slot) pairs by local expert.
-// launch_align: one work-group; E <= 1024. launch_align_multi: the same result
+// launch_align: one work-group; E <= 512. launch_align_multi: the same result
 // from many work-groups (three launches), with align_scratch_ints(P, E) int32
 // of scratch.
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
