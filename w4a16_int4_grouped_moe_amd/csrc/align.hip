@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 //        expert (bucket offset + pairs of that expert in earlier chunks), and
 //        writes n_padded, the padding and the block map.
 // scatter: each wave places its chunk's pairs exactly as the single-group
-//        kernel does (ranks from ballots), from its own cursors.
+//        kernel does (ranks from LDS lane masks), from its own cursors.
 // The result is identical to the single-group kernel's.
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / 64;
