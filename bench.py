@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "skew", "ep", "tp8_decode", "tp8_prefill",
                              "tiny"])
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="token count of a single-batch workload (default: the workload's own)")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens per batch of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -187,7 +189,7 @@ def main():
     if args.workload in ("decode", "tp8_decode"):
         batches = [1, 8, 32, 64]
     else:
-        batches = [mi.workload(args.workload).T]
+        batches = [args.tokens or mi.workload(args.workload).T]
     w0 = mi.workload(args.workload, batches[0])
     g = w0.geo
     t_setup = time.perf_counter()

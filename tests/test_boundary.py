@@ -66,10 +66,13 @@ def P(**kw):
 def test_workspace_size_and_block_m(lib):
     p = P()
     assert moe.forward_block_m(p) == 4
-    assert moe.forward_block_m(P(num_tokens=512)) == 16
+    assert moe.forward_block_m(P(num_tokens=192)) == 4     # T k = 4 E
+    assert moe.forward_block_m(P(num_tokens=193)) == 96
+    assert moe.forward_block_m(P(num_tokens=512)) == 96
     assert moe.forward_block_m(P(num_tokens=4096)) == 96
-    assert moe.forward_block_m(P(num_tokens=4096, hidden=7040)) == 64  # 7040 % 256 != 0
-    assert moe.forward_block_m(P(num_tokens=2048)) == 64
+    # widths the prefill kernel's tiles do not fit (7040 % 512 != 0)
+    assert moe.forward_block_m(P(num_tokens=512, hidden=7040)) == 16
+    assert moe.forward_block_m(P(num_tokens=4096, hidden=7040)) == 64
     # one GPU's share of an 8-way tensor-parallel split (intermediate 256)
     assert moe.forward_block_m(P(inter=256)) == 4
     assert moe.forward_block_m(P(inter=256, num_tokens=4096)) == 96

@@ -9,21 +9,27 @@ from tests.helpers import run_layer
 
 pytestmark = pytest.mark.gpu
 
-H, I, E, K = 512, 256, 16, 4
+E, K = 16, 4
+# (tokens, hidden, inter): 16-row blocks of the tiled kernel (widths the prefill
+# kernel's tiles do not fit), 4-row blocks, and prefill blocks
+SHAPES = {"tiled": (96, 640, 384), "small-batch": (8, 512, 256), "prefill": (300, 512, 256)}
 
 
-@pytest.fixture(scope="module", params=[96, 8, 300], ids=["tiled", "small-batch", "prefill"])
+@pytest.fixture(scope="module", params=sorted(SHAPES))
 def setup(request):
     import torch
+    import w4a16_int4_grouped_moe_amd as moe
 
-    T = request.param
+    T, H, I = SHAPES[request.param]
+    want = {"tiled": 16, "small-batch": 4, "prefill": 96}[request.param]
+    assert moe.forward_block_m(moe.problem(T, H, I, E, K)) == want
     dev = torch.device("cuda:0")
     bank = mi.weight_bank(3, H, I, list(range(E)))
     bank_dev = {k: mi.to_device(v, dev) for k, v in bank.__dict__.items()}
     x = mi.activations(4, T, H)
     ids, w = mi.routing_uniform(5, T, E, K)
     sw = mi.shared_weights(3, H, I)
-    return dev, bank, bank_dev, x, ids, w, sw
+    return dev, bank, bank_dev, x, ids, w, sw, H, I
 
 
 def bits(t):
@@ -34,14 +40,14 @@ def bits(t):
 
 
 def test_deterministic(setup):
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     a = bits(run_layer(dev, x, ids, w, bank_dev, sw))
     for _ in range(10):
         assert np.array_equal(bits(run_layer(dev, x, ids, w, bank_dev, sw)), a)
 
 
 def test_zero_weights_and_invalid_ids_give_shared_only(setup):
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     a = bits(run_layer(dev, x, ids, np.zeros_like(w), bank_dev, sw))
     b = bits(run_layer(dev, x, np.full_like(ids, -1), w, bank_dev, sw))
     c = bits(run_layer(dev, x, ids + E, w, bank_dev, sw))  # all ids beyond the local range
@@ -54,7 +60,7 @@ def test_zero_weights_and_invalid_ids_give_shared_only(setup):
 def test_doubling_down_scales_doubles_output_exactly(setup):
     import torch
 
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     base = run_layer(dev, x, ids, w, bank_dev, None)
     doubled_dev = dict(bank_dev)
     doubled_dev["scales_w2"] = bank_dev["scales_w2"] * 2
@@ -66,7 +72,7 @@ def test_doubling_down_scales_doubles_output_exactly(setup):
 def test_token_permutation(setup):
     import torch
 
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     perm = np.random.default_rng(1).permutation(x.shape[0])
     a = run_layer(dev, x, ids, w, bank_dev, sw).float()
     b = run_layer(dev, x[perm], ids[perm], w[perm], bank_dev, sw).float()
@@ -79,7 +85,7 @@ def test_empty_batch(setup):
 
     import w4a16_int4_grouped_moe_amd as moe
 
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     out = run_layer(dev, x[:0], ids[:0], w[:0], bank_dev, sw)
     assert out.shape == (0, H)
     p = moe.problem(0, H, I, E, K)
@@ -91,7 +97,7 @@ def test_graph_capture_replay(setup):
 
     import w4a16_int4_grouped_moe_amd as moe
 
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     d = lambda a: mi.to_device(a, dev)
     xs, ids_d, w_d, sw_d = d(x), d(ids), d(w), d(sw)
     T = x.shape[0]
@@ -126,7 +132,7 @@ def test_timed_entry_point(setup):
     import ctypes
     import torch
 
-    dev, bank, bank_dev, x, ids, w, sw = setup
+    dev, bank, bank_dev, x, ids, w, sw, H, I = setup
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,

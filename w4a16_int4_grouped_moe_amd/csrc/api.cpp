@@ -40,13 +40,14 @@ int64_t sorted_capacity(const moe_w4a16_problem* p, int32_t bm) {
 
 int32_t choose_block_m(const moe_w4a16_problem* p) {
   // About one row per expert (decode): 4-row buckets and the weight-streaming
-  // small-batch kernels. Many rows per expert (prefill): the prefill kernel's
-  // blocks, or 64-row blocks where its tiles do not fit the widths. In
-  // between: 16-row blocks.
+  // small-batch kernels. Beyond that, the prefill kernel's blocks wherever its
+  // tiles fit the widths (measured faster than 16- and 64-row blocks from a
+  // few rows per expert on, and with skewed routing); else 64-row blocks with
+  // many rows per expert and 16-row blocks in between.
   const int64_t P = p->num_tokens * p->top_k;
   const int64_t E = p->num_experts;
   if (P <= 4 * E && moe::small_batch_fits(p->hidden, p->inter)) return 4;
-  if (P >= 64 * E && moe::prefill_fits(p->hidden, p->inter)) return moe::prefill_block_m();
+  if (moe::prefill_fits(p->hidden, p->inter)) return moe::prefill_block_m();
   return P >= 32 * E ? 64 : 16;
 }
 
