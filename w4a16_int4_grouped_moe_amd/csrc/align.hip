@@ -12,18 +12,19 @@
 //      do not depend on order);
 //   2. per expert: prefix of the wave counts, padded size, block-wide scan of
 //      the padded sizes -> bucket offsets and n_padded;
-//   3. each wave walks its chunk 64 pairs at a time in pair order; the lanes
+//   3. sentinel padding and block_expert (the scatter never writes these
+//      positions);
+//   4. each wave walks its chunk 64 pairs at a time in pair order; the lanes
 //      of a step that share an expert are ranked by lane: each lane ORs its
 //      bit into the expert's 64-bit lane mask in a per-wave LDS table (an OR
 //      does not depend on order), reads the mask back and counts the lower
-//      lanes, so positions are exactly the stable order;
-//   4. sentinel padding and block_expert.
+//      lanes, so positions are exactly the stable order.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 512;  // at least MOE_MAX_EXPERTS: thread e owns expert e in the scans
+constexpr int kThreads = kMaxExperts;  // thread e owns expert e in the scans
 constexpr int kWaves = kThreads / 64;
 
 // The lanes of this wave that hold expert e (e < 0: none), as a lane mask:
@@ -39,6 +40,60 @@ __device__ __forceinline__ uint64_t lane_group(uint64_t* wmask, int e, int lane)
 
 __device__ __forceinline__ void clear_lane_group(uint64_t* wmask, int e) {
   __hip_atomic_store(&wmask[e], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Sentinel padding of each bucket and the block -> expert map, by all the
+// work-group's threads (tid of nthreads = 64 nwaves; E <= nthreads).
+// off/cnt: bucket start (a multiple of bm) and valid pairs, in LDS.
+// sorted_ids must be 16-byte aligned.
+//
+// Blocks of at most kPadPerThread rows: thread e pads its own bucket (at most
+// bm - 1 entries) and writes its blocks.
+// Larger blocks: a padding of up to bm - 1 entries per thread would take as
+// many serial stores, each to a cache line per lane. Instead a wave splits
+// into 8 groups of 8 lanes; group g takes the wave's experts g, g + 8, ...
+// (expert wave + nwaves (8 i + g)), and its lanes cover the padding in
+// aligned 4-entry windows, lane j windows j, j + 8, ...: a whole window with
+// one 16-byte store, the (at most two) partial ones entry by entry.
+constexpr int kPadPerThread = 16;
+
+__device__ __forceinline__ void pad_buckets(const int32_t* off, const int32_t* cnt, int E, int bm,
+                                            int32_t sentinel, int tid, int nwaves,
+                                            int32_t* __restrict__ sorted_ids,
+                                            int32_t* __restrict__ block_expert) {
+  if (bm <= kPadPerThread) {
+    if (tid < E) {
+      const int o = off[tid];
+      const int c = cnt[tid];
+      const int nb = (c + bm - 1) / bm;
+      for (int r = c; r < nb * bm; ++r) sorted_ids[o + r] = sentinel;
+      const int b0 = o / bm;
+      for (int b = 0; b < nb; ++b) block_expert[b0 + b] = tid;
+    }
+    return;
+  }
+  const int wave = tid >> 6, g = (tid >> 3) & 7, j = tid & 7;
+  const int4 fill = make_int4(sentinel, sentinel, sentinel, sentinel);
+  for (int i = 0; wave + nwaves * 8 * i < E; ++i) {
+    const int e = wave + nwaves * (8 * i + g);
+    if (e >= E) continue;
+    const int o = off[e];
+    const int c = cnt[e];
+    const int nb = (c + bm - 1) / bm;
+    const int start = o + c, end = o + nb * bm;
+    for (int w = (start >> 2) + j; 4 * w < end; w += 8) {
+      const int a = 4 * w;
+      if (a >= start && a + 4 <= end) {
+        *reinterpret_cast<int4*>(sorted_ids + a) = fill;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (a + u >= start && a + u < end) sorted_ids[a + u] = sentinel;
+      }
+    }
+    const int b0 = o / bm;
+    for (int b = j; b < nb; b += 8) block_expert[b0 + b] = e;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void align_kernel(
@@ -112,7 +167,10 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   for (int i = tid; i < kWaves * E; i += kThreads) hist[i] += off[i % E];
   __syncthreads();
 
-  // 3. stable scatter, 64 pairs at a time in pair order
+  // 3. sentinel padding and the block map (positions the scatter never writes)
+  pad_buckets(off, cnt, E, bm, (int32_t)P, tid, kWaves, sorted_ids, block_expert);
+
+  // 4. stable scatter, 64 pairs at a time in pair order
   uint64_t* const wmask = masks + wave * E;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t p0 = c0; p0 < c1; p0 += 64) {
@@ -134,26 +192,18 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
       }
     }
   }
-  __syncthreads();
-
-  // 4. padding and the block map
-  if (tid < E) {
-    const int o = off[tid];
-    const int c = cnt[tid];
-    const int pd = (c + bm - 1) / bm * bm;
-    for (int r = c; r < pd; ++r) sorted_ids[o + r] = (int32_t)P;
-    for (int b = o / bm; b < (o + pd) / bm; ++b) block_expert[b] = tid;
-  }
 }
 
 // ---- many work-groups (large P): count, scan, scatter ----------------------
 // The pairs are cut into chunks of kChunk consecutive pairs, one per wave.
 // count: each wave histograms its chunk into counts[chunk][E] (plain stores).
-// scan:  one work-group turns the counts into each chunk's first position per
-//        expert (bucket offset + pairs of that expert in earlier chunks), and
-//        writes n_padded, the padding and the block map.
+// scan:  one work-group turns the counts into each chunk's pairs of that
+//        expert in earlier chunks (in place), stores the bucket offsets after
+//        them (scratch[nq * E + e]), and writes n_padded, the padding and the
+//        block map.
 // scatter: each wave places its chunk's pairs exactly as the single-group
-//        kernel does (ranks from LDS lane masks), from its own cursors.
+//        kernel does (ranks from LDS lane masks), from its own cursors
+//        (bucket offset + earlier pairs).
 // The result is identical to the single-group kernel's.
 constexpr int kMultiThreads = 256;
 constexpr int kMultiWaves = kMultiThreads / 64;
@@ -184,6 +234,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
     int64_t P, int E, int bm, int32_t* __restrict__ counts, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ n_padded_out) {
   __shared__ int32_t wsum[16];
+  __shared__ int32_t off_s[kMaxExperts], cnt_s[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nq = (P + kChunk - 1) / kChunk;
   // per expert: exclusive prefix over the chunks (in place), total; sixteen
@@ -223,10 +274,12 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(
   const int off = incl - pad + (wave > 0 ? wsum[wave - 1] : 0);
   if (tid == 1023) *n_padded_out = off + pad;
   if (tid < E) {
-    for (int64_t q = 0; q < nq; ++q) counts[q * E + tid] += off;
-    for (int r = run; r < pad; ++r) sorted_ids[off + r] = (int32_t)P;
-    for (int b = off / bm; b < (off + pad) / bm; ++b) block_expert[b] = tid;
+    counts[nq * E + tid] = off;
+    off_s[tid] = off;
+    cnt_s[tid] = run;
   }
+  __syncthreads();
+  pad_buckets(off_s, cnt_s, E, bm, (int32_t)P, tid, 16, sorted_ids, block_expert);
 }
 
 __global__ __launch_bounds__(kMultiThreads) void align_scatter_kernel(
@@ -240,7 +293,7 @@ __global__ __launch_bounds__(kMultiThreads) void align_scatter_kernel(
   const int64_t nq = (P + kChunk - 1) / kChunk;
   for (int i = tid; i < kMultiWaves * E; i += kMultiThreads) {
     const int64_t qq = (int64_t)blockIdx.x * kMultiWaves + i / E;
-    cur[i] = qq < nq ? cursors[qq * E + i % E] : 0;
+    cur[i] = qq < nq ? cursors[nq * E + i % E] + cursors[qq * E + i % E] : 0;
     masks[i] = 0;
   }
   __syncthreads();
@@ -273,7 +326,7 @@ __global__ __launch_bounds__(kMultiThreads) void align_scatter_kernel(
 }  // namespace
 
 int64_t align_scratch_ints(int64_t P, int32_t E) {
-  return (P + kChunk - 1) / kChunk * E;
+  return ((P + kChunk - 1) / kChunk + 1) * E;
 }
 
 hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,

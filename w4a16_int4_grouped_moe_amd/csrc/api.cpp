@@ -17,6 +17,9 @@ thread_local char g_status_msg[256];
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+static_assert(moe::kMaxExperts == MOE_MAX_EXPERTS,
+              "the bucketing kernels size their tables for MOE_MAX_EXPERTS");
+
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 int check_problem(const moe_w4a16_problem* p) {
@@ -52,7 +55,10 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
 }
 
 // Bucketing in many work-groups (three launches) from this many pairs on.
-constexpr int64_t kAlignMultiMin = 8192;
+#ifndef MOE_ALIGN_MULTI_MIN
+#define MOE_ALIGN_MULTI_MIN 8192
+#endif
+constexpr int64_t kAlignMultiMin = MOE_ALIGN_MULTI_MIN;
 
 struct Layout {
   size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, shared_gu, blas, total;

@@ -8,9 +8,10 @@
 namespace moe {
 
 // Bucketing: stable counting sort of valid (token, slot) pairs by local expert.
-// launch_align: one work-group; E <= 512. launch_align_multi: the same result
-// from many work-groups (three launches), with align_scratch_ints(P, E) int32
-// of scratch.
+// launch_align: one work-group; E <= kMaxExperts. launch_align_multi: the
+// same result from many work-groups (three launches), with
+// align_scratch_ints(P, E) int32 of scratch.
+constexpr int kMaxExperts = 512;
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* n_padded, hipStream_t stream);
