@@ -125,7 +125,8 @@ int moe_w4a16_align(const int32_t *topk_ids, const moe_w4a16_problem *p, int32_t
 
 /*
  * Scratch bytes (host out) of the many-work-group bucketing for this problem:
- * one int32 per (chunk of 256 pairs, local expert).
+ * one int32 per (chunk of 256 pairs, local expert), plus one per local
+ * expert (the bucket offsets).
  */
 int moe_w4a16_align_scratch_size(const moe_w4a16_problem *p, size_t *bytes);
 

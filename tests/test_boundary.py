@@ -162,7 +162,7 @@ def test_align_argument_errors(lib):
     assert call(npad=None) == moe.MOE_ERR_NULL
     assert call(sorted=f(0x20004)) == moe.MOE_ERR_ALIGNMENT
     need = moe.align_scratch_size(p)
-    assert need == 4 * ((p.num_tokens * p.top_k + 255) // 256) * p.num_experts
+    assert need == 4 * ((p.num_tokens * p.top_k + 255) // 256 + 1) * p.num_experts
     assert call(scratch=f(0x50000), nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(scratch=f(0x50008), nbytes=need) == moe.MOE_ERR_ALIGNMENT
     with pytest.raises(ValueError):
