@@ -32,6 +32,8 @@
 // sum x * (u - 8); the group's bf16 scale then multiplies it in fp32 (the
 // weight is never rounded). The bf16 shared expert uses the same structure
 // with its weights taken as they are (natural order, no scales).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace moe {
@@ -168,6 +170,52 @@ constexpr int stage_bytes() { return NB * kXBytes; }
 __host__ __device__ inline int scale_row_bytes(int K) {
   const int niters = (K / 32 + kGroupsPerIt - 1) / kGroupsPerIt;
   return 32 * (niters | 1);
+}
+
+// One iteration of an int4 work item: 16 groups of K against NR row-sets of
+// four weight rows (w: this lane's code words, group kp of row j of each
+// row-set), activations from the LDS stage of the iteration, each group's
+// scale from sread (row-set rs at + 4 rs srow, iteration it at + 32 it).
+template <int NR>
+__device__ __forceinline__ void int4_step(const u32x4 (&w)[NR], const uint8_t* stage,
+                                          const uint8_t* sread, int srow, int it,
+                                          f32x4 (&acc)[NR]) {
+  const int lane = threadIdx.x & 63;
+  u32x4 xf[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xf[q] = *reinterpret_cast<const u32x4*>(stage + q * 1024 + lane * 16);
+  // C0 = -136 * (sum of the group's activations), per token row
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
+  const u32x2 neg136 = {kNeg136, kNeg136};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c0 = mfma4(u32x2{xf[q][0], xf[q][1]}, neg136, c0);
+    c0 = mfma4(u32x2{xf[q][2], xf[q][3]}, neg136, c0);
+  }
+  // NR independent chains, interleaved so that consecutive MFMAs never
+  // depend on each other
+  f32x4 t[NR];
+#pragma unroll
+  for (int rs = 0; rs < NR; ++rs) t[rs] = c0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x2 b0[NR], b1[NR];
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) {
+      const uint32_t v = w[rs][q];
+      b0[rs] = u32x2{and_or(v, 0x000F000Fu, kMagic), and_or(v >> 4, 0x000F000Fu, kMagic)};
+      b1[rs] = u32x2{and_or(v >> 8, 0x000F000Fu, kMagic), and_or(v >> 12, 0x000F000Fu, kMagic)};
+    }
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) t[rs] = mfma4(u32x2{xf[q][0], xf[q][1]}, b0[rs], t[rs]);
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) t[rs] = mfma4(u32x2{xf[q][2], xf[q][3]}, b1[rs], t[rs]);
+  }
+#pragma unroll
+  for (int rs = 0; rs < NR; ++rs) {
+    const uint32_t sb = *reinterpret_cast<const uint16_t*>(sread + rs * 4 * srow + it * 32);
+    acc[rs] += bf16_to_f32(sb) * t[rs];
+  }
 }
 
 // NB blocks of four rows starting at row0 (NB > 1 only for the bf16 shared
@@ -360,43 +408,10 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 
   auto compute = [&](const Frag& f, const uint8_t* stage, int it) {
     if (INT4) {
-      u32x4 xf[4];
+      u32x4 w[NR];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        xf[q] = *reinterpret_cast<const u32x4*>(stage + q * 1024 + lane * 16);
-      // C0 = -136 * (sum of the group's activations), per token row
-      f32x4 c0 = {0.f, 0.f, 0.f, 0.f};
-      const u32x2 neg136 = {kNeg136, kNeg136};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c0 = mfma4(u32x2{xf[q][0], xf[q][1]}, neg136, c0);
-        c0 = mfma4(u32x2{xf[q][2], xf[q][3]}, neg136, c0);
-      }
-      // NR independent chains, interleaved so that consecutive MFMAs never
-      // depend on each other
-      f32x4 t[NR];
-#pragma unroll
-      for (int rs = 0; rs < NR; ++rs) t[rs] = c0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x2 b0[NR], b1[NR];
-#pragma unroll
-        for (int rs = 0; rs < NR; ++rs) {
-          const uint32_t w = f.w[rs][0][q];
-          b0[rs] = u32x2{and_or(w, 0x000F000Fu, kMagic), and_or(w >> 4, 0x000F000Fu, kMagic)};
-          b1[rs] = u32x2{and_or(w >> 8, 0x000F000Fu, kMagic),
-                         and_or(w >> 12, 0x000F000Fu, kMagic)};
-        }
-#pragma unroll
-        for (int rs = 0; rs < NR; ++rs) t[rs] = mfma4(u32x2{xf[q][0], xf[q][1]}, b0[rs], t[rs]);
-#pragma unroll
-        for (int rs = 0; rs < NR; ++rs) t[rs] = mfma4(u32x2{xf[q][2], xf[q][3]}, b1[rs], t[rs]);
-      }
-#pragma unroll
-      for (int rs = 0; rs < NR; ++rs) {
-        const uint32_t sb = *reinterpret_cast<const uint16_t*>(sread + rs * 4 * srow + it * 32);
-        acc[0][rs] += bf16_to_f32(sb) * t[rs];
-      }
+      for (int rs = 0; rs < NR; ++rs) w[rs] = f.w[rs][0];
+      int4_step<NR>(w, stage, sread, srow, it, acc[0]);
     } else {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
@@ -538,6 +553,241 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kerne
     const int s = (int)(b2 - blk * wg_slices);
     if (blk * 4 >= *p.n_padded) return;
     small_tile<PHASE, NR, true, 1, kSmallDepth>(p, blk * 4, s * kWaves, lds);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streamed down projection (int4 part) for 512 < K <= 2048, e.g. I = 2048.
+// With K that short, a work item of small_tile runs only K / 512 iterations
+// between its prologue (staging, first loads) and its epilogue, and the
+// stream drains at every item. Here a work-group takes nsg consecutive slice
+// groups (4 NR x 4 weight rows each) of one 4-row bucket block instead: the
+// block's activations for all of K are staged in LDS once, the scales per
+// slice group (double buffered, one barrier per slice group), and the weight
+// prefetch runs on across slice groups, so that the stream does not stop
+// until the work-group's last rows. Arithmetic and numerics are small_tile's.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxIters = 4;  // K <= 2048: every activation stage in LDS at once
+#ifndef MOE_STREAM_SG
+#define MOE_STREAM_SG 4
+#endif
+constexpr int kStreamSG = MOE_STREAM_SG;  // most slice groups per work-group
+
+template <int NR>
+constexpr int stream_rows() { return kWaves * 4 * NR; }  // weight rows of a slice group
+
+template <int NR>
+int stream_lds_bytes(int K) {
+  const int niters = (K / 32 + kGroupsPerIt - 1) / kGroupsPerIt;
+  return niters * kXBytes + 2 * stream_rows<NR>() * scale_row_bytes(K);
+}
+
+template <int NR, int DEPTH>
+__device__ __forceinline__ void down_stream_tile(const GemmParams& p, int64_t row0, int sg0,
+                                                 int nsg, uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kp = lane >> 2;
+  const int j = lane & 3;
+  const int K = p.K;
+  const int ngroups = K / 32;
+  const int niters = (ngroups + kGroupsPerIt - 1) / kGroupsPerIt;  // <= kStreamMaxIters
+  const int tail = ngroups % kGroupsPerIt;
+  constexpr int kRows = stream_rows<NR>();
+  const int srow = scale_row_bytes(K);
+  const int rowbytes = K / 2;
+  uint8_t* const act = lds;  // [niters][kXBytes]
+  uint8_t* const sbuf = lds + niters * kXBytes;  // [2][kRows][srow]
+
+  const int e = p.block_expert[row0 / 4];
+  const int64_t r0 = (int64_t)e * p.N;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + r0 * (K / 8)), 0, p.N * rowbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.scales + r0 * (K / 32)), 0, p.N * (K / 32) * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_routed, 0, (int)((int64_t)p.max_blocks * 4 * K * 2), kBufferFlags);
+
+  // this lane's weights in slice group 0: row-set rs, row j, group kp
+  int woff[NR];
+#pragma unroll
+  for (int rs = 0; rs < NR; ++rs)
+    woff[rs] = ((sg0 * kRows + wave * 4 * NR + 4 * rs + j) * (K / 8) + 4 * kp) * 4;
+  // the prefetch position (slice group, iteration) and its loads; past the
+  // work-group's last iteration an offset beyond the buffer (reads zeros)
+  int pf_sg = 0, pf_it = 0;
+  auto load_next = [&](u32x4 (&w)[NR]) {
+    const int off = uniform(pf_sg < nsg ? pf_sg * kRows * rowbytes + pf_it * (kGroupsPerIt * 16)
+                                        : kOutOfRange);
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs)
+      w[rs] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], off, kStreamAux);
+    if (++pf_it == niters) {
+      pf_it = 0;
+      ++pf_sg;
+    }
+  };
+
+  // scales of slice group sg: kRows rows x 2 niters pieces of 16 bytes
+  const int ppr = 2 * niters;
+  const int npieces = kRows * ppr;
+  constexpr int kSP = (kRows * 2 * kStreamMaxIters + kThreads - 1) / kThreads;
+  u32x4 sv[kSP];
+  auto load_scales = [&](int sg) {
+#pragma unroll
+    for (int u = 0; u < kSP; ++u) {
+      const int i = u * kThreads + tid;
+      const int r = i / ppr, pc = i - r * ppr;
+      int off = kOutOfRange;
+      if (i < npieces && pc * 8 < ngroups) off = (((sg0 + sg) * kRows + r) * (K / 32) + pc * 8) * 2;
+      sv[u] = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, kScaleAux);
+    }
+  };
+  auto store_scales = [&](uint8_t* sb) {
+#pragma unroll
+    for (int u = 0; u < kSP; ++u) {
+      const int i = u * kThreads + tid;
+      if (i < npieces) {
+        const int r = i / ppr, pc = i - r * ppr;
+        const int valid = ngroups - pc * 8;  // groups of the piece inside K
+        u32x4 v = sv[u];
+        if (valid < 8) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t lo = 2 * h < valid ? (v[h] & 0xFFFFu) : 0u;
+            const uint32_t hi = 2 * h + 1 < valid ? (v[h] & 0xFFFF0000u) : 0u;
+            v[h] = lo | hi;
+          }
+        }
+        *reinterpret_cast<u32x4*>(sb + r * srow + pc * 16) = v;
+      }
+    }
+  };
+
+  struct Frag {
+    u32x4 w[NR];
+  };
+  Frag f[DEPTH + 1];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    load_next(f[d].w);
+    __builtin_amdgcn_sched_barrier(0);  // keep the iterations' loads in issue order
+  }
+
+  // activations of the block for all of K: thread t -> token row t / 64,
+  // piece t % 64 of each iteration's 1 KB (the fragment slots of small_tile)
+  const int xt = tid >> 6;
+  const int xc = tid & 63;
+  const int xoff = (int)((row0 + xt) * K) * 2 + xc * 16;
+  u32x4 xv[kStreamMaxIters];
+#pragma unroll
+  for (int it = 0; it < kStreamMaxIters; ++it)
+    xv[it] = __builtin_amdgcn_raw_buffer_load_b128(xres, xoff,
+                                                   uniform(it < niters ? it * 1024 : kOutOfRange), 0);
+  load_scales(0);
+  // the pair of token row r = kp % 4 (every slice group stores to it)
+  const int r = kp & 3;
+  const int32_t pair = p.sorted_ids[row0 + r];
+  float* const dst = pair < p.P ? p.y_routed + (int64_t)pair * p.N : nullptr;
+
+  const int xdst = (xc & 3) * 1024 + ((xc >> 2) * 4 + xt) * 16;
+#pragma unroll
+  for (int it = 0; it < kStreamMaxIters; ++it) {
+    if (it >= niters) break;
+    u32x4 v = xv[it];
+    if (tail && it == niters - 1 && (xc >> 2) >= tail) v = u32x4{0, 0, 0, 0};
+    // (x0..x7) -> (x0,x4,x1,x5 | x2,x6,x3,x7), the codes' field order
+    v = u32x4{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
+              __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+              __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
+              __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+    *reinterpret_cast<u32x4*>(act + it * kXBytes + xdst) = v;
+  }
+  store_scales(sbuf);
+  if (nsg > 1) load_scales(1);  // in flight during slice group 0
+  __syncthreads();
+
+  f32x4 acc[NR];
+#pragma unroll
+  for (int rs = 0; rs < NR; ++rs) acc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's scales: row (wave, 4 rs + j), group kp of the iteration
+  const int sread_off = (wave * 4 * NR + j) * srow + kp * 2;
+
+  // sum the k-parts of slice group sg and store its 4 NR columns per wave
+  auto finish = [&](int sg) {
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[rs][q] = kpart_sum(acc[rs][q]);
+    const int col0 = ((sg0 + sg) * kWaves + wave) * (4 * NR);
+#pragma unroll
+    for (int t = 0; t < (NR + 3) / 4; ++t) {
+      const int rsd = (kp >> 2) + 4 * t;
+      if (rsd >= NR) continue;
+      float v = 0.f;
+#pragma unroll
+      for (int rs = 0; rs < NR; ++rs) {
+        if (rs == rsd) {
+          v = acc[rs][0];
+          v = (r == 1) ? acc[rs][1] : v;
+          v = (r == 2) ? acc[rs][2] : v;
+          v = (r == 3) ? acc[rs][3] : v;
+        }
+      }
+      if (dst) dst[col0 + 4 * rsd + j] = v;
+    }
+#pragma unroll
+    for (int rs = 0; rs < NR; ++rs) acc[rs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  constexpr int kPeriod = (DEPTH + 1) % 2 ? 2 * (DEPTH + 1) : DEPTH + 1;
+  const int total = nsg * niters;
+  int it = 0, sg = 0;
+  for (int i0 = 0; i0 < total; i0 += kPeriod) {
+#pragma unroll
+    for (int u = 0; u < kPeriod; ++u) {
+      load_next(f[(u + DEPTH) % (DEPTH + 1)].w);
+      __builtin_amdgcn_sched_barrier(0);
+      int4_step<NR>(f[u % (DEPTH + 1)].w, act + it * kXBytes,
+                    sbuf + (sg & 1) * kRows * srow + sread_off, srow, it, acc);
+      if (++it == niters) {
+        finish(sg);
+        it = 0;
+        ++sg;
+        if (sg < nsg) {
+          store_scales(sbuf + (sg & 1) * kRows * srow);
+          __syncthreads();
+          if (sg + 1 < nsg) load_scales(sg + 1);
+        }
+      }
+      if (i0 + u + 1 >= total) break;
+    }
+  }
+}
+
+// Shared-expert work-groups first (as in small_gemm_kernel), then routed ones:
+// each 4-row bucket block is split into runs of `sgs` slice groups.
+template <int NR, int NRS, int TB>
+__global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void stream_down_kernel(GemmParams p,
+                                                                                   int sgs) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // stream_down_lds_bytes
+  const int64_t bid = blockIdx.x;
+  const int ns = p.N / slice_cols<kDown, NRS>() / kWaves;
+  const int64_t shared = p.wshared ? (p.T + 4 * TB - 1) / (4 * TB) * ns : 0;
+  if (bid < shared) {
+    const int64_t tg = bid / ns;
+    const int s = (int)(bid - tg * ns);
+    small_tile<kDown, NRS, false, TB, 1>(p, tg * 4 * TB, s * kWaves, lds);
+  } else {
+    const int groups = p.N / stream_rows<NR>();
+    const int runs = (groups + sgs - 1) / sgs;
+    const int64_t b2 = bid - shared;
+    const int64_t blk = b2 / runs;
+    const int q = (int)(b2 - blk * runs);
+    if (blk * 4 >= *p.n_padded) return;
+    const int sg0 = q * sgs;
+    down_stream_tile<NR, kSmallDepth>(p, blk * 4, sg0, min(sgs, groups - sg0), lds);
   }
 }
 
@@ -874,6 +1124,36 @@ hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
   return launch_small_tb<PHASE, NR, NRS, kTokBlocks>(p, stream);
 }
 
+// Streamed down launch. Slice groups per routed work-group: enough routed
+// work-groups to hold about kStreamTargetWG of them (the bucket count is not
+// known on the host; min(pairs, experts) estimates it), at most kStreamSG.
+constexpr int64_t kStreamTargetWG = 2048;
+
+template <int NR, int NRS, int TB>
+hipError_t launch_stream_down(const GemmParams& p, hipStream_t stream) {
+  if (p.N % stream_rows<NR>() || p.N % (slice_cols<kDown, NRS>() * kWaves) || p.K % 32)
+    return hipErrorInvalidValue;
+  const int routed_lds = stream_lds_bytes<NR>(p.K);
+  const int shared_lds = 2 * stage_bytes<TB>();
+  const int lds = routed_lds > shared_lds ? routed_lds : shared_lds;
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  const int groups = p.N / stream_rows<NR>();
+  const int64_t est_blocks = std::max<int64_t>(1, std::min<int64_t>(p.P, p.max_blocks));
+  int sgs = (int)std::min<int64_t>(kStreamSG, est_blocks * groups / kStreamTargetWG);
+  if (sgs < 1) sgs = 1;
+  const int64_t routed = (int64_t)p.max_blocks * ((groups + sgs - 1) / sgs);
+  const int64_t shared = p.wshared ? (p.T + 4 * TB - 1) / (4 * TB) *
+                                         (p.N / slice_cols<kDown, NRS>() / kWaves)
+                                   : 0;
+  const int64_t grid = routed + shared;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  GemmParams args = p;
+  void* kargs[] = {&args, &sgs};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_down_kernel<NR, NRS, TB>),
+                         dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
+}
+
 }  // namespace
 
 bool small_batch_fits(int32_t hidden, int32_t inter) {
@@ -888,6 +1168,10 @@ hipError_t launch_down_small(const GemmParams& p, hipStream_t stream) {
   if (p.K <= 128) return launch_narrow<4>(p, stream);
   if (p.K <= 256) return launch_narrow<8>(p, stream);
   if (p.K <= 512) return launch_narrow<16>(p, stream);
+  if (p.K <= 32 * kGroupsPerIt * kStreamMaxIters) {
+    if (p.T > 4 * kTokBlocks) return launch_stream_down<kNRDown, kNRS, kTokBlocksLarge>(p, stream);
+    return launch_stream_down<kNRDown, kNRS, kTokBlocks>(p, stream);
+  }
   return launch_small<kDown, kNRDown, kNRS>(p, stream);
 }
 
