@@ -1,6 +1,7 @@
 """Layer parity over a spread of shapes that reach every kernel path and its
 edges: K not a multiple of the small-batch iteration (partial last
 iteration), down widths that take the narrow-K kernel (I = 128, 384), the
+streamed down kernel with several slice groups per work-group, the
 largest top-k (16) and expert count (512), expert bases with non-local ids,
 ragged token counts, and each block size (4, 16, 64, 96).
 
@@ -24,6 +25,7 @@ CASES = [
     (5, 1152, 640, 6, 3, 1, False, 4),     # K = 1152 and a down K of 640 (partial iterations)
     (1, 384, 128, 16, 16, 0, True, 4),     # top-16, narrow down (I = 128)
     (8, 256, 128, 512, 8, 0, True, 4),     # 512 local experts
+    (120, 2048, 640, 128, 4, 0, True, 4),  # streamed down: 3 slice groups per work-group, last run of 2
     (33, 640, 384, 8, 4, 0, True, 16),     # 16-row blocks, ragged T
     (97, 384, 640, 6, 2, 2, True, 64),     # 64-row blocks, expert base
     (700, 1536, 512, 10, 2, 0, True, 96),  # prefill blocks, shared expert in the library GEMM
