@@ -28,6 +28,7 @@ CASES = [
     (120, 2048, 640, 128, 4, 0, True, 4),  # streamed down: 3 slice groups per work-group, last run of 2
     (33, 640, 384, 8, 4, 0, True, 16),     # 16-row blocks, ragged T
     (97, 384, 640, 6, 2, 2, True, 64),     # 64-row blocks, expert base
+    (150, 1024, 512, 8, 2, 1, True, 96),   # prefill blocks, expert base
     (700, 1536, 512, 10, 2, 0, True, 96),  # prefill blocks, shared expert in the library GEMM
     (160, 1024, 768, 4, 3, 0, False, 96),  # prefill blocks, no shared expert, I = 768
 ]
