@@ -104,7 +104,8 @@ class Hip:
 
 def traffic_record(workload):
     """rocprofv3 FETCH_SIZE / WRITE_SIZE of the gate_up kernel, if the record in
-    profiles/ was taken on the current gemm.hip."""
+    profiles/ was taken on the current GEMM sources (workload: the record's
+    name, e.g. "prefill" or "prefill_prepacked")."""
     h = hashlib.sha256()
     for f in GEMM_SRCS:
         h.update(open(f, "rb").read())
@@ -169,6 +170,9 @@ def main():
                     help="tokens per batch of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time of the CPU-oracle sample (repeated passes)")
+    ap.add_argument("--prepacked", action="store_true",
+                    help="run the layer on prepacked weights (moe_w4a16_prepack, once per "
+                         "weight copy, before the timed region)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -220,9 +224,21 @@ def main():
     print(f"[bench] setup {t_setup:.1f} s; workload {args.workload} batches {batches}",
           file=sys.stderr, flush=True)
 
+    if args.prepacked:
+        for c in calls:  # the weight copies are replaced by their prepacked form
+            a = c["args"]
+            c["pk"] = moe.prepack(a[3], a[4], a[5], a[6])
+            c["args"] = a[:3] + (None, None, None, None) + a[7:]
+        torch.cuda.synchronize()
+
     def run(c, events=None):
-        moe.forward(*c["args"], out=c["out"], expert_base=c["base"], workspace=c["ws"],
-                    stage_events=events)
+        if args.prepacked:
+            x, ids, wts = c["args"][:3]
+            moe.forward_prepacked(x, ids, wts, c["pk"], c["args"][7], out=c["out"],
+                                  expert_base=c["base"], workspace=c["ws"], stage_events=events)
+        else:
+            moe.forward(*c["args"], out=c["out"], expert_base=c["base"], workspace=c["ws"],
+                        stage_events=events)
 
     for _ in range(args.warmup):
         for c in calls:
@@ -272,6 +288,43 @@ def main():
         torch.cuda.synchronize()
         route_us.append(float(np.median([a.elapsed_time(b) for a, b in ev[1:]])) * 1e3)
 
+    # the same steps with the weights in prepacked form (moe_w4a16_prepack, a
+    # one-time load step outside the timing), where the widths allow it; the
+    # headline above stays on the checkpoint-layout weights the layer's entry
+    # point takes
+    prepacked = None
+    if not args.prepacked:
+        try:
+            pks = [moe.prepack(*c["args"][3:7]) for c in calls]
+        except (ValueError, moe.MoeError):
+            pks = None
+        if pks:
+            def run_pk(c, pk, ev=None):
+                x, ids, wts = c["args"][:3]
+                moe.forward_prepacked(x, ids, wts, pk, c["args"][7], out=c["out"],
+                                      expert_base=c["base"], workspace=c["ws"], stage_events=ev)
+
+            for _ in range(args.warmup):
+                for c, pk in zip(calls, pks):
+                    run_pk(c, pk)
+            ev_pk = [[[None, hip.event(), None, None, None, hip.event(), None] for _ in calls]
+                     for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            for step in range(args.steps):
+                for c, pk, ev in zip(calls, pks, ev_pk[step]):
+                    run_pk(c, pk, ev)
+            torch.cuda.synchronize()
+            ms_pk = (time.perf_counter() - t2) * 1e3 / args.steps
+            prepacked = {
+                "value": round(tokens_per_step / (ms_pk / 1e3), 1), "ms_per_step": round(ms_pk, 4),
+                "gate_up_us": [round(float(np.mean([hip.elapsed_ms(ev_pk[s][ci][1], ev_pk[s][ci][5])
+                                                    for s in range(args.steps)])) * 1e3, 2)
+                               for ci in range(len(calls))],
+                "note": "same steps with the weights prepacked once (moe_w4a16_prepack) and "
+                        "moe_w4a16_forward_prepacked; results identical bit for bit"}
+            del pks
+
     stage_names = ["align", "gate_up", "down", "combine"]
     per_batch = []
     gate_up_ms, gate_up_bytes, gate_up_flops = [], [], []
@@ -303,7 +356,7 @@ def main():
     # dominant kernel: the gate_up GEMM (two thirds of the routed weight bytes
     # and of the FLOPs); per-launch averages over the timed steps
     mean_s = float(np.mean(gate_up_ms)) / 1e3
-    rec = traffic_record(args.workload)
+    rec = traffic_record(args.workload + ("_prepacked" if args.prepacked else ""))
     traffic = None
     if rec is not None:
         traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
@@ -357,12 +410,14 @@ def main():
         "data": "synthetic (seeded: int4 codes uniform, bf16 scales U(0.005,0.02), "
                 "x N(0,1), uniform distinct top-k routing, softmax weights)",
         "config": {"workload": wl, "batches": batches, "hidden": g.hidden, "inter": g.inter,
+                   "weights": "prepacked" if args.prepacked else "checkpoint layout",
                    "experts": w0.n_local, "top_k": g.top_k, "shared_expert": g.shared,
                    "block_m": [moe.forward_block_m(moe.problem(T, g.hidden, g.inter, w0.n_local,
                                                                g.top_k)) for T in batches]},
         "per_batch": per_batch,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "prepacked": prepacked,
     }
     print(json.dumps(line), flush=True)
 

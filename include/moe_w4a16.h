@@ -211,6 +211,57 @@ int moe_w4a16_forward_scores(const void *x, const float *scores, int32_t num_sco
                              size_t workspace_bytes, void *stream);
 
 /*
+ * Prepacked weights: the weight-loading step that the lmdeploy "support Kimi
+ * K2.6" pull request (Changes list) names for the compressed-tensors W4A16
+ * experts, done once ahead of the layer calls. The same int4 codes and bf16
+ * scales, reordered so that the prefill kernel's reads take whole cache lines
+ * (the order is internal to the library and may change between versions;
+ * only moe_w4a16_prepack writes it and only the *_prepacked calls read it).
+ * Results are bit for bit those of moe_w4a16_forward on the original weights.
+ *
+ * Supported widths: hidden % 512 == 0, inter % 256 == 0 and inter > 512
+ * (e.g. the full Kimi-K2.6 layer, 7168 / 2048); others give
+ * MOE_ERR_UNSUPPORTED (use moe_w4a16_forward). The buffer depends on
+ * hidden, inter and num_experts only.
+ *
+ * moe_w4a16_prepack_size: bytes of the prepacked buffer (host only; about the
+ * size of packed_w13 + scales_w13 + packed_w2 + scales_w2).
+ */
+int moe_w4a16_prepack_size(const moe_w4a16_problem *p, size_t *bytes);
+
+/*
+ * Writes the prepacked form of the four weight tensors (layouts as in
+ * moe_w4a16_forward) into `prepacked` (device, prepacked_bytes long, at least
+ * moe_w4a16_prepack_size), on `stream`. The inputs are only read and may be
+ * freed once the stream work has completed. MOE_ERR_WORKSPACE if the buffer
+ * is too small; the other errors as for moe_w4a16_forward.
+ */
+int moe_w4a16_prepack(const int32_t *packed_w13, const void *scales_w13,
+                      const int32_t *packed_w2, const void *scales_w2,
+                      const moe_w4a16_problem *p, void *prepacked, size_t prepacked_bytes,
+                      void *stream);
+
+/*
+ * moe_w4a16_forward with the weights in prepacked form (written by
+ * moe_w4a16_prepack for the same hidden, inter and num_experts); every other
+ * argument, the workspace size and the results as for moe_w4a16_forward.
+ * MOE_ERR_WORKSPACE if prepacked_bytes is below moe_w4a16_prepack_size.
+ */
+int moe_w4a16_forward_prepacked(const void *x, const int32_t *topk_ids,
+                                const float *topk_weights, const void *prepacked,
+                                size_t prepacked_bytes, const void *shared_w, void *out,
+                                const moe_w4a16_problem *p, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* moe_w4a16_forward_prepacked with the stage events of moe_w4a16_forward_timed. */
+int moe_w4a16_forward_prepacked_timed(const void *x, const int32_t *topk_ids,
+                                      const float *topk_weights, const void *prepacked,
+                                      size_t prepacked_bytes, const void *shared_w, void *out,
+                                      const moe_w4a16_problem *p, void *workspace,
+                                      size_t workspace_bytes, void *stream,
+                                      void *const *stage_events);
+
+/*
  * A static description of `status`; for MOE_ERR_HIP it names the HIP error
  * of the failing call on this thread. Never NULL.
  */

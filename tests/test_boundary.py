@@ -33,6 +33,8 @@ def test_header_declares_expected_entry_points():
         "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_align_scratch_size",
         "moe_w4a16_forward",
         "moe_w4a16_forward_block_m", "moe_w4a16_forward_scores", "moe_w4a16_forward_timed",
+        "moe_w4a16_forward_prepacked", "moe_w4a16_forward_prepacked_timed",
+        "moe_w4a16_prepack", "moe_w4a16_prepack_size",
         "moe_w4a16_route", "moe_w4a16_status_string", "moe_w4a16_workspace_size"])
 
 
@@ -209,3 +211,67 @@ def test_route_argument_errors(lib):
     bad = list(args)
     bad[2] = 2000
     assert lib.moe_w4a16_forward_scores(*bad, need, None) == moe.MOE_ERR_SHAPE
+
+
+def test_prepack_sizes_and_supported_widths(lib):
+    # the full layer: the prepacked form is exactly as large as the four tensors
+    per_expert = (2 * 2048 * 7168 // 2 + 2 * 2048 * 7168 // 32 * 2 +
+                  7168 * 2048 // 2 + 7168 * 2048 // 32 * 2)
+    assert moe.prepack_size(7168, 2048, 384) == 384 * per_expert
+    # hidden 512, inter 768, 3 experts: W13 rows hold 16 scale groups (one
+    # period of 16), W2 rows 24 (two periods, the second padded); regions are
+    # 256-byte aligned
+    rnd = lambda v: (v + 255) // 256 * 256
+    codes13, scales13 = 3 * 1536 * 512 // 2, 3 * 1536 * 1 * 32
+    codes2, scales2 = 3 * 512 * 768 // 2, 3 * 512 * 2 * 32
+    assert moe.prepack_size(512, 768, 3) == (rnd(codes13) + rnd(scales13) + rnd(codes2) +
+                                             rnd(scales2))
+    # widths the layout does not serve: the narrow down kernel's (inter <= 512),
+    # and widths the prefill tiles do not fit
+    for hidden, inter in ((7168, 256), (7168, 512), (640, 1024), (1024, 640)):
+        n = ctypes.c_size_t()
+        pp = P(hidden=hidden, inter=inter)
+        assert lib.moe_w4a16_prepack_size(ctypes.byref(pp), ctypes.byref(n)) == \
+            moe.MOE_ERR_UNSUPPORTED, (hidden, inter)
+
+
+def test_prepack_argument_errors_before_launch(lib):
+    p = P(num_experts=4)
+    need = moe.prepack_size(7168, 2048, 4)
+    w = [ctypes.c_void_p(0x10000 + 0x100 * i) for i in range(4)]
+    buf = ctypes.c_void_p(0x90000)
+    call = lambda ptrs, b=buf, n=need, pp=p: lib.moe_w4a16_prepack(*ptrs, ctypes.byref(pp), b, n,
+                                                                   None)
+    for i in range(4):
+        ptrs = list(w)
+        ptrs[i] = None
+        assert call(ptrs) == moe.MOE_ERR_NULL, i
+        ptrs[i] = ctypes.c_void_p(0x10008)
+        assert call(ptrs) == moe.MOE_ERR_ALIGNMENT, i
+    assert call(w, b=None) == moe.MOE_ERR_NULL
+    assert call(w, b=ctypes.c_void_p(0x90004)) == moe.MOE_ERR_ALIGNMENT
+    assert call(w, n=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(w, pp=P(num_experts=4, inter=256)) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_forward_prepacked_argument_errors_before_launch(lib):
+    p = P(num_experts=4)
+    need = moe.prepack_size(7168, 2048, 4)
+    ws = moe.workspace_size(p)
+    x, ids, wts, sw, out = (ctypes.c_void_p(0x10000 + 0x100 * i) for i in range(5))
+    buf = ctypes.c_void_p(0x90000)
+
+    def call(b=buf, n=need, x=x, ids=ids, wts=wts, out=out, wsp=ctypes.c_void_p(0x20000),
+             wsn=ws, pp=p):
+        return lib.moe_w4a16_forward_prepacked(x, ids, wts, b, n, sw, out, ctypes.byref(pp), wsp,
+                                               wsn, None)
+
+    assert call(b=None) == moe.MOE_ERR_NULL
+    assert call(b=ctypes.c_void_p(0x90008)) == moe.MOE_ERR_ALIGNMENT
+    assert call(n=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(x=None) == moe.MOE_ERR_NULL
+    assert call(out=ctypes.c_void_p(0x10004)) == moe.MOE_ERR_ALIGNMENT
+    assert call(wsn=ws - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(pp=P(num_experts=4, inter=256)) == moe.MOE_ERR_UNSUPPORTED
+    # zero tokens: a no-op that touches no pointer
+    assert call(b=None, x=None, pp=P(num_tokens=0, num_experts=4)) == moe.MOE_OK

@@ -8,6 +8,8 @@ PyTorch supplies device memory and the current stream.
                   packed_w2, scales_w2, shared_w=None, out=None, expert_base=0)
     ids, weights = route(scores, top_k)              # router step
     out, ids, weights = forward_scores(x, scores, top_k, packed_w13, ...)
+    pk = prepack(packed_w13, scales_w13, packed_w2, scales_w2)   # once
+    out = forward_prepacked(x, topk_ids, topk_weights, pk, shared_w=None)
 """
 from ._binding import (  # noqa: F401
     MOE_ERR_ALIGNMENT,
@@ -19,14 +21,18 @@ from ._binding import (  # noqa: F401
     MOE_OK,
     LIB_PATH,
     MoeError,
+    Prepacked,
     Problem,
     align,
     align_capacity,
     align_scratch_size,
     forward,
     forward_block_m,
+    forward_prepacked,
     forward_scores,
     library,
+    prepack,
+    prepack_size,
     problem,
     route,
     status_string,

@@ -66,11 +66,18 @@ def library():
         lib.moe_w4a16_route.argtypes = [P, ctypes.c_int32, PP, P, P, P]
         lib.moe_w4a16_forward_scores.argtypes = ([P, P, ctypes.c_int32] + [P] * 8 +
                                                  [PP, P, ctypes.c_size_t, P])
+        lib.moe_w4a16_prepack_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+        lib.moe_w4a16_prepack.argtypes = [P] * 4 + [PP, P, ctypes.c_size_t, P]
+        lib.moe_w4a16_forward_prepacked.argtypes = ([P] * 3 + [P, ctypes.c_size_t, P, P] +
+                                                    [PP, P, ctypes.c_size_t, P])
+        lib.moe_w4a16_forward_prepacked_timed.argtypes = (
+            [P] * 3 + [P, ctypes.c_size_t, P, P] + [PP, P, ctypes.c_size_t, P, P])
         lib.moe_w4a16_status_string.argtypes = [ctypes.c_int]
         lib.moe_w4a16_status_string.restype = ctypes.c_char_p
         for f in ("workspace_size", "forward_block_m", "align_capacity", "align",
                   "align_scratch_size", "forward", "forward_timed", "route",
-                  "forward_scores"):
+                  "forward_scores", "prepack_size", "prepack", "forward_prepacked",
+                  "forward_prepacked_timed"):
             getattr(lib, "moe_w4a16_" + f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -223,6 +230,102 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
             raise ValueError("stage_events needs 7 entries")
         ev = (ctypes.c_void_p * 7)(*[e or None for e in stage_events])
         st = library().moe_w4a16_forward_timed(*args, ev)
+    _check(st)
+    return out
+
+
+class Prepacked:
+    """Expert weights in the library's prepacked form (moe_w4a16_prepack):
+    a uint8 device buffer and the widths it was written for."""
+
+    def __init__(self, buffer, hidden: int, inter: int, num_experts: int):
+        self.buffer = buffer
+        self.hidden = hidden
+        self.inter = inter
+        self.num_experts = num_experts
+
+
+def prepack_size(hidden: int, inter: int, num_experts: int) -> int:
+    """Bytes of the prepacked form of num_experts experts (host only)."""
+    n = ctypes.c_size_t()
+    _check(library().moe_w4a16_prepack_size(
+        ctypes.byref(problem(0, hidden, inter, num_experts, 1)), ctypes.byref(n)))
+    return n.value
+
+
+def prepack(packed_w13, scales_w13, packed_w2, scales_w2, out=None) -> Prepacked:
+    """One-time repack of the four weight tensors (layouts as for forward)
+    into the prepacked form that forward_prepacked reads; out: an optional
+    uint8 device buffer of at least prepack_size bytes."""
+    torch = _torch()
+    dev = packed_w13.device
+    if dev.type != "cuda":
+        raise ValueError("the weights must be GPU tensors")
+    _need(packed_w13, "packed_w13", torch.int32, 3, dev)
+    E, I2, H8 = packed_w13.shape
+    H, I = 8 * H8, I2 // 2
+    for name, t, dtype, shape in (("scales_w13", scales_w13, torch.bfloat16, (E, 2 * I, H // GROUP)),
+                                  ("packed_w2", packed_w2, torch.int32, (E, H, I // 8)),
+                                  ("scales_w2", scales_w2, torch.bfloat16, (E, H, I // GROUP))):
+        _need(t, name, dtype, 3, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    need = prepack_size(H, I, E)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        _need(out, "out", torch.uint8, 1, dev)
+    p = problem(0, H, I, E, 1)
+    _check(library().moe_w4a16_prepack(
+        packed_w13.data_ptr(), scales_w13.data_ptr(), packed_w2.data_ptr(),
+        scales_w2.data_ptr(), ctypes.byref(p), out.data_ptr(), out.numel(),
+        _stream_handle(dev)))
+    return Prepacked(out, H, I, E)
+
+
+def forward_prepacked(x, topk_ids, topk_weights, prepacked: Prepacked, shared_w=None, out=None,
+                      expert_base: int = 0, workspace=None, stage_events=None):
+    """forward with the expert weights in prepacked form (see prepack); the
+    same results, bit for bit."""
+    torch = _torch()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    _need(x, "x", torch.bfloat16, 2, dev)
+    _need(topk_ids, "topk_ids", torch.int32, 2, dev)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if H != prepacked.hidden:
+        raise ValueError(f"x has width {H}, the prepacked weights {prepacked.hidden}")
+    I, E = prepacked.inter, prepacked.num_experts
+    _need(prepacked.buffer, "prepacked.buffer", torch.uint8, 1, dev)
+    if shared_w is not None:
+        _need(shared_w, "shared_w", torch.bfloat16, 1, dev)
+        if shared_w.numel() != 3 * I * H:
+            raise ValueError(f"shared_w must hold {3 * I * H} values")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, 2, dev)
+        if tuple(out.shape) != (T, H):
+            raise ValueError("out must be [T, H]")
+    _routing(topk_ids, topk_weights, T, k, dev)
+    p = problem(T, H, I, E, k, expert_base)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(p), 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    args = (x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(),
+            prepacked.buffer.data_ptr(), prepacked.buffer.numel(),
+            None if shared_w is None else shared_w.data_ptr(), out.data_ptr(), ctypes.byref(p),
+            workspace.data_ptr(), workspace.numel(), _stream_handle(dev))
+    if stage_events is None:
+        st = library().moe_w4a16_forward_prepacked(*args)
+    else:
+        if len(stage_events) != 7:
+            raise ValueError("stage_events needs 7 entries")
+        ev = (ctypes.c_void_p * 7)(*[e or None for e in stage_events])
+        st = library().moe_w4a16_forward_prepacked_timed(*args, ev)
     _check(st)
     return out
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_w4a16.so")
-SOURCES = ["align.hip", "route.hip", "gemm.hip", "gemm_small.hip", "gemm_prefill.hip", "combine.hip",
+SOURCES = ["align.hip", "route.hip", "gemm.hip", "gemm_small.hip", "gemm_prefill.hip", "prepack.hip", "combine.hip",
            "shared_blas.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

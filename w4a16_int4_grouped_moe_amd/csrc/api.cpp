@@ -193,7 +193,8 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
                         const int32_t* packed_w13, const void* scales_w13,
                         const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
                         void* out, const moe_w4a16_problem* p, void* workspace,
-                        size_t workspace_bytes, void* stream, void* const* events) {
+                        size_t workspace_bytes, void* stream, void* const* events,
+                        bool prepacked = false) {
   const int st = check_forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2,
                                scales_w2, shared_w, out, p, workspace, workspace_bytes);
   if (st != MOE_OK || p->num_tokens == 0) return st;
@@ -271,6 +272,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.k = k;
   g.I = I;
   g.nibble_mask = 0x0F0F0F0Fu;
+  g.prepacked = prepacked ? 1 : 0;
 
   // gate_up + SwiGLU
   g.a_routed = static_cast<const uint16_t*>(x);
@@ -324,6 +326,103 @@ int moe_w4a16_forward_timed(const void* x, const int32_t* topk_ids, const float*
                             void* const* stage_events) {
   return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
                       shared_w, out, p, workspace, workspace_bytes, stream, stage_events);
+}
+
+// ---- prepacked weights --------------------------------------------------------
+// Buffer: W13 codes, W13 scales, W2 codes, W2 scales of all local experts, each
+// region 256-byte aligned, in the layout of internal.h.
+struct PackLayout {
+  size_t w13, s13, w2, s2, total;
+};
+
+static PackLayout pack_layout(const moe_w4a16_problem* p) {
+  const size_t E = (size_t)p->num_experts;
+  const int32_t H = p->hidden, I = p->inter;
+  PackLayout L{};
+  size_t o = 0;
+  L.w13 = o; o = round_up(o + E * (size_t)moe::pack_code_bytes(2 * I, H));
+  L.s13 = o; o = round_up(o + E * (size_t)moe::pack_scale_bytes(2 * I, H));
+  L.w2 = o; o = round_up(o + E * (size_t)moe::pack_code_bytes(H, I));
+  L.s2 = o; o = round_up(o + E * (size_t)moe::pack_scale_bytes(H, I));
+  L.total = o;
+  return L;
+}
+
+// Widths the prepacked layout serves: every batch size must run on the
+// small-batch and prefill kernels, which read it (the tiled kernel and the
+// narrow down kernel for inter <= 512 do not).
+static int check_prepack_problem(const moe_w4a16_problem* p) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!moe::prefill_fits(p->hidden, p->inter) || p->inter <= 512) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_w4a16_prepack_size(const moe_w4a16_problem* p, size_t* bytes) {
+  const int st = check_prepack_problem(p);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = pack_layout(p).total;
+  return MOE_OK;
+}
+
+int moe_w4a16_prepack(const int32_t* packed_w13, const void* scales_w13,
+                      const int32_t* packed_w2, const void* scales_w2,
+                      const moe_w4a16_problem* p, void* prepacked, size_t prepacked_bytes,
+                      void* stream) {
+  const int st = check_prepack_problem(p);
+  if (st != MOE_OK) return st;
+  if (!packed_w13 || !scales_w13 || !packed_w2 || !scales_w2 || !prepacked) return MOE_ERR_NULL;
+  const void* ptrs[] = {packed_w13, scales_w13, packed_w2, scales_w2, prepacked};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return MOE_ERR_ALIGNMENT;
+  const PackLayout L = pack_layout(p);
+  if (prepacked_bytes < L.total) return MOE_ERR_WORKSPACE;
+  uint8_t* b = static_cast<uint8_t*>(prepacked);
+  const int32_t E = p->num_experts, H = p->hidden, I = p->inter;
+  hipStream_t strm = (hipStream_t)stream;
+  hipError_t err = moe::launch_prepack(packed_w13, static_cast<const uint16_t*>(scales_w13), E,
+                                       2 * I, H, true, I, b + L.w13, b + L.s13, strm);
+  if (err != hipSuccess) return hip_status(err);
+  return hip_status(moe::launch_prepack(packed_w2, static_cast<const uint16_t*>(scales_w2), E, H,
+                                        I, false, I, b + L.w2, b + L.s2, strm));
+}
+
+static int forward_prepacked_impl(const void* x, const int32_t* topk_ids,
+                                  const float* topk_weights, const void* prepacked,
+                                  size_t prepacked_bytes, const void* shared_w, void* out,
+                                  const moe_w4a16_problem* p, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* const* events) {
+  const int st = check_prepack_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->num_tokens == 0) return MOE_OK;
+  if (!prepacked) return MOE_ERR_NULL;
+  if (!aligned16(prepacked)) return MOE_ERR_ALIGNMENT;
+  const PackLayout L = pack_layout(p);
+  if (prepacked_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const uint8_t* b = static_cast<const uint8_t*>(prepacked);
+  return forward_impl(x, topk_ids, topk_weights, reinterpret_cast<const int32_t*>(b + L.w13),
+                      b + L.s13, reinterpret_cast<const int32_t*>(b + L.w2), b + L.s2, shared_w,
+                      out, p, workspace, workspace_bytes, stream, events, true);
+}
+
+int moe_w4a16_forward_prepacked(const void* x, const int32_t* topk_ids,
+                                const float* topk_weights, const void* prepacked,
+                                size_t prepacked_bytes, const void* shared_w, void* out,
+                                const moe_w4a16_problem* p, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return forward_prepacked_impl(x, topk_ids, topk_weights, prepacked, prepacked_bytes, shared_w,
+                                out, p, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_w4a16_forward_prepacked_timed(const void* x, const int32_t* topk_ids,
+                                      const float* topk_weights, const void* prepacked,
+                                      size_t prepacked_bytes, const void* shared_w, void* out,
+                                      const moe_w4a16_problem* p, void* workspace,
+                                      size_t workspace_bytes, void* stream,
+                                      void* const* stage_events) {
+  return forward_prepacked_impl(x, topk_ids, topk_weights, prepacked, prepacked_bytes, shared_w,
+                                out, p, workspace, workspace_bytes, stream, stage_events);
 }
 
 static int check_route(const float* scores, int32_t num_scored, const moe_w4a16_problem* p,

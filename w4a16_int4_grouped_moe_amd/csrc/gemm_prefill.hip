@@ -76,6 +76,7 @@ constexpr int kWBytes = kBN * kWRowBytes;
 constexpr int kSRowBytes = kSPeriod * 4 * 2;  // scale bytes of one row per buffer
 constexpr int kSBytes = kBN * kSRowBytes;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
+static_assert(kBN == kPackRows && kKC == kPackChunk, "tiles of the prepacked layout");
 constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
 
 enum { kGateUp = 0, kDown = 1 };
@@ -219,6 +220,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   };
 
   // ---- weight copies: instruction u covers rows 16u..16u+15 (64 B each) ------
+  // Checkpoint layout: row R's 64 bytes of chunk ch at ch * 64 in its row of
+  // K / 2 bytes. Prepacked layout: the tile's chunk is one 32 KB run (rows of
+  // 64 bytes), so an instruction reads 1 KB of whole lines.
+  const bool packed_layout = p.prepacked != 0;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + wbase * (K / 8)), 0, Nw * (K / 8) * 4, kBufferFlags);
   uint32_t woff[4];
@@ -226,10 +231,13 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   for (int i = 0; i < 4; ++i) {
     const int R = 16 * (4 * wave + i) + (lane >> 2);
     const int g = (lane & 3) ^ wslot(R);
-    woff[i] = (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 8) + 4 * g) * 4);
+    woff[i] = packed_layout
+                  ? (uint32_t)(((tile * nch) * kBN + R) * kWRowBytes + 16 * g)
+                  : (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 8) + 4 * g) * 4);
   }
+  const int wstep = packed_layout ? kWBytes : kWRowBytes;  // bytes per chunk
   auto copy_w = [&](uint8_t* dst, int ch) {
-    const int so = uniform(ch < nch ? ch * kWRowBytes : (int)kNoRow);
+    const int so = uniform(ch < nch ? ch * wstep : (int)kNoRow);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(dst + (4 * wave + i) * 1024), 16,
@@ -237,17 +245,28 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   };
 
   // ---- scale copies: instruction v covers rows 32v..32v+31 (32 B each) -------
-  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.scales + wbase * (K / 32)), 0, Nw * (K / 32) * 2, kBufferFlags);
+  // (prepacked: a period of the tile is one 16 KB run; its periods are the
+  // four-chunk periods here)
+  static_assert(kSPeriod * kKC == 16 * 32, "scale periods of the prepacked layout");
+  const int nper = (nch + kSPeriod - 1) / kSPeriod;
+  const __amdgpu_buffer_rsrc_t sres =
+      packed_layout
+          ? __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(reinterpret_cast<const uint8_t*>(p.scales) + e * pack_scale_bytes(Nw, K)),
+                0, (int)pack_scale_bytes(Nw, K), kBufferFlags)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + wbase * (K / 32)), 0,
+                                              Nw * (K / 32) * 2, kBufferFlags);
   uint32_t soff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int R = 32 * (2 * wave + i) + (lane >> 1);
-    soff[i] = (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 32) + 8 * (lane & 1)) * 2);
+    soff[i] = packed_layout
+                  ? (uint32_t)(((tile * nper) * kBN + R) * kSRowBytes + 16 * (lane & 1))
+                  : (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 32) + 8 * (lane & 1)) * 2);
   }
-  const int nper = (nch + kSPeriod - 1) / kSPeriod;
+  const int sstep = packed_layout ? kSBytes : kSRowBytes;  // bytes per period
   auto copy_s = [&](uint8_t* dst, int per) {
-    const int so = uniform(per < nper ? per * kSRowBytes : (int)kNoRow);
+    const int so = uniform(per < nper ? per * sstep : (int)kNoRow);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_ptr)(dst + (2 * wave + i) * 1024), 16,

@@ -281,10 +281,19 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
   const int srow = scale_row_bytes(K);
   uint8_t* const slds = lds + 2 * stage_bytes<NB>();
   const int e = INT4 ? p.block_expert[row0 / 4] : 0;
+  // prepacked weights (see internal.h): tiles of kPackRows rows, each 128-input
+  // chunk of a tile and each 16-group scale period of it one contiguous run
+  const bool packed_layout = INT4 && p.prepacked != 0;
   auto stage_scales = [&]() {
     const int64_t r0 = (int64_t)e * Nw;
-    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.scales + r0 * (K / 32)), 0, Nw * (K / 32) * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t sres =
+        packed_layout
+            ? __builtin_amdgcn_make_buffer_rsrc(
+                  (void*)(reinterpret_cast<const uint8_t*>(p.scales) +
+                          e * pack_scale_bytes(Nw, K)),
+                  0, (int)pack_scale_bytes(Nw, K), kBufferFlags)
+            : __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
+                                                Nw * (K / 32) * 2, kBufferFlags);
     const int ppr = 2 * niters;  // pieces per row
     const int npieces = kRowsWG * ppr;
     auto batch = [&](int base) {
@@ -299,7 +308,9 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
         int off = kOutOfRange;
         if (i < npieces && pc * 8 < ngroups) {
           const int w = r / (4 * NR), lr = r % (4 * NR);
-          off = (weight_row<PHASE, NR>(p, slice0 + w, lr / 4, lr % 4) * (K / 32) + pc * 8) * 2;
+          const int n = weight_row<PHASE, NR>(p, slice0 + w, lr / 4, lr % 4);
+          off = packed_layout ? (int)pack_scale_offset(PHASE == kGateUp, p.I, K, n, pc * 8)
+                              : (n * (K / 32) + pc * 8) * 2;
         }
         v[u] = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, kScaleAux);
       }
@@ -340,12 +351,18 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
   } else {
     wres = __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
   }
+  // lane (kp, j): group kp of iteration it of row j of each row-set; the
+  // iteration adds wstep bytes (checkpoint layout: 16 groups of the row;
+  // prepacked: four chunks of the tile)
   int woff[NR];
 #pragma unroll
   for (int rs = 0; rs < NR; ++rs) {
     const int row = weight_row<PHASE, NR>(p, slice, rs, j);
-    woff[rs] = INT4 ? (row * (K / 8) + 4 * kp) * 4 : (row * K + 32 * kp) * 2;
+    woff[rs] = !INT4          ? (row * K + 32 * kp) * 2
+               : packed_layout ? (int)pack_code_offset(PHASE == kGateUp, p.I, K, row, kp)
+                               : (row * (K / 8) + 4 * kp) * 4;
   }
+  const int wstep = packed_layout ? (kGroupsPerIt / 4) * kPackRows * 64 : kGroupsPerIt * 16;
   // this lane's scales: row (wave, 4 rs + j), group kp of the iteration
   const uint8_t* const sread = slds + (wave * 4 * NR + j) * srow + kp * 2;
 
@@ -362,7 +379,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) {
       if (INT4) {
-        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], kofs(it, kGroupsPerIt * 16),
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], kofs(it, wstep),
                                                            kStreamAux);
       } else {
 #pragma unroll
@@ -602,24 +619,45 @@ __device__ __forceinline__ void down_stream_tile(const GemmParams& p, int64_t ro
 
   const int e = p.block_expert[row0 / 4];
   const int64_t r0 = (int64_t)e * p.N;
+  const bool packed_layout = p.prepacked != 0;  // see internal.h
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + r0 * (K / 8)), 0, p.N * rowbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.scales + r0 * (K / 32)), 0, p.N * (K / 32) * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sres =
+      packed_layout
+          ? __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(reinterpret_cast<const uint8_t*>(p.scales) + e * pack_scale_bytes(p.N, K)),
+                0, (int)pack_scale_bytes(p.N, K), kBufferFlags)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
+                                              p.N * (K / 32) * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a_routed, 0, (int)((int64_t)p.max_blocks * 4 * K * 2), kBufferFlags);
 
-  // this lane's weights in slice group 0: row-set rs, row j, group kp
+  // this lane's weights: row-set rs, row j, group kp. Checkpoint layout: the
+  // offset in slice group 0, plus kRows rows per slice group and 16 groups per
+  // iteration. Prepacked layout (down rows in tiles of kPackRows, kRows
+  // dividing it): the offset inside a slice group's rows of a tile, plus the
+  // slice group's place (its tile, its rows in the tile) and four chunks of
+  // the tile per iteration.
+  static_assert(kPackRows % kRows == 0, "slice groups inside prepacked tiles");
   int woff[NR];
 #pragma unroll
-  for (int rs = 0; rs < NR; ++rs)
-    woff[rs] = ((sg0 * kRows + wave * 4 * NR + 4 * rs + j) * (K / 8) + 4 * kp) * 4;
+  for (int rs = 0; rs < NR; ++rs) {
+    const int l = wave * 4 * NR + 4 * rs + j;  // row inside the slice group
+    woff[rs] = packed_layout ? (int)pack_code_offset(false, 0, K, l, kp)
+                             : ((sg0 * kRows + l) * (K / 8) + 4 * kp) * 4;
+  }
+  auto group_base = [&](int sg) {  // uniform: bytes of slice group sg0 + sg
+    if (!packed_layout) return sg * kRows * rowbytes;
+    const int sgg = sg0 + sg;
+    constexpr int kPerTile = kPackRows / kRows;
+    return (sgg / kPerTile) * pack_chunks(K) * kPackRows * 64 + (sgg % kPerTile) * kRows * 64;
+  };
+  const int wstep = packed_layout ? (kGroupsPerIt / 4) * kPackRows * 64 : kGroupsPerIt * 16;
   // the prefetch position (slice group, iteration) and its loads; past the
   // work-group's last iteration an offset beyond the buffer (reads zeros)
   int pf_sg = 0, pf_it = 0;
   auto load_next = [&](u32x4 (&w)[NR]) {
-    const int off = uniform(pf_sg < nsg ? pf_sg * kRows * rowbytes + pf_it * (kGroupsPerIt * 16)
-                                        : kOutOfRange);
+    const int off = uniform(pf_sg < nsg ? group_base(pf_sg) + pf_it * wstep : kOutOfRange);
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs)
       w[rs] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], off, kStreamAux);
@@ -640,7 +678,11 @@ __device__ __forceinline__ void down_stream_tile(const GemmParams& p, int64_t ro
       const int i = u * kThreads + tid;
       const int r = i / ppr, pc = i - r * ppr;
       int off = kOutOfRange;
-      if (i < npieces && pc * 8 < ngroups) off = (((sg0 + sg) * kRows + r) * (K / 32) + pc * 8) * 2;
+      if (i < npieces && pc * 8 < ngroups) {
+        const int n = (sg0 + sg) * kRows + r;
+        off = packed_layout ? (int)pack_scale_offset(false, 0, K, n, pc * 8)
+                            : (n * (K / 32) + pc * 8) * 2;
+      }
       sv[u] = __builtin_amdgcn_raw_buffer_load_b128(sres, off, 0, kScaleAux);
     }
   };

@@ -47,7 +47,60 @@ struct GemmParams {
   int32_t I;                    // intermediate width
   int32_t N;                    // output width (I for gate_up, H for down)
   uint32_t nibble_mask;         // 0x0F0F0F0F (a run-time value on purpose)
+  int32_t prepacked;            // packed/scales in the prepacked layout (below)
 };
+
+// ---- prepacked weights ------------------------------------------------------
+// The layout moe_w4a16_prepack writes, per expert and matrix (W13: Nw = 2I
+// rows, K = H; W2: Nw = H, K = I). Rows are grouped in tiles of kPackRows (the
+// prefill kernel's work-group rows; W13 rows in the order that kernel takes
+// them: per 64-row wave slice, 16 gate rows, the next 16 gate rows, then the
+// 32 matching up rows). Within a tile:
+//   codes:  [K / 128 chunks][kPackRows rows][4 groups x 16 bytes]
+//   scales: [ceil(K / 512) periods][kPackRows rows][16 groups x 2 bytes],
+//           zero past the last group
+// so that each 128-input chunk of a tile (32 KB of codes), and each 16-group
+// period of its scales (16 KB), is contiguous. Requires Nw % kPackRows == 0
+// and K % 128 == 0.
+constexpr int kPackRows = 512;
+constexpr int kPackChunk = 128;  // inputs per chunk
+
+struct PackPos {
+  int32_t tile, row;  // tile of the weight row and its row inside the tile
+};
+__host__ __device__ inline PackPos pack_pos(bool w13, int32_t I, int32_t n) {
+  if (!w13) return PackPos{n / kPackRows, n % kPackRows};
+  const int32_t up = n >= I ? 2 : 0;
+  const int32_t c = up ? n - I : n;
+  const int32_t cc = c % (kPackRows / 2);
+  const int32_t w = cc / 32, s = (cc % 32) / 16 + up, r = cc % 16;
+  return PackPos{c / (kPackRows / 2), 64 * w + 16 * s + r};
+}
+__host__ __device__ inline int32_t pack_chunks(int32_t K) { return K / kPackChunk; }
+__host__ __device__ inline int32_t pack_periods(int32_t K) { return (K / 32 + 15) / 16; }
+// bytes of one expert's codes / scales
+__host__ __device__ inline int64_t pack_code_bytes(int32_t Nw, int32_t K) {
+  return (int64_t)Nw * (K / 2);
+}
+__host__ __device__ inline int64_t pack_scale_bytes(int32_t Nw, int32_t K) {
+  return (int64_t)Nw * pack_periods(K) * 32;
+}
+// byte offset (inside one expert) of group g (32 inputs) of weight row n
+__host__ __device__ inline int64_t pack_code_offset(bool w13, int32_t I, int32_t K, int32_t n,
+                                                    int32_t g) {
+  const PackPos q = pack_pos(w13, I, n);
+  return (((int64_t)q.tile * pack_chunks(K) + g / 4) * kPackRows + q.row) * 64 + 16 * (g % 4);
+}
+__host__ __device__ inline int64_t pack_scale_offset(bool w13, int32_t I, int32_t K, int32_t n,
+                                                     int32_t g) {
+  const PackPos q = pack_pos(w13, I, n);
+  return (((int64_t)q.tile * pack_periods(K) + g / 16) * kPackRows + q.row) * 32 + 2 * (g % 16);
+}
+// One-time repack of an int4 matrix [E, Nw, K/8] and its bf16 scales
+// [E, Nw, K/32] into the layout above.
+hipError_t launch_prepack(const int32_t* packed, const uint16_t* scales, int32_t E, int32_t Nw,
+                          int32_t K, bool w13, int32_t I, uint8_t* codes_out,
+                          uint8_t* scales_out, hipStream_t stream);
 
 hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stream);
 hipError_t launch_down(const GemmParams& p, int32_t block_m, hipStream_t stream);
