@@ -172,7 +172,7 @@ __device__ __forceinline__ int weight_row(const GemmParams& p, int tile, int R) 
   return tile * kBN + w * 64 + 16 * s + r;
 }
 
-template <int PHASE, int MS>
+template <int PHASE, int MS, bool PK>
 __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int tile) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,7 +223,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // Checkpoint layout: row R's 64 bytes of chunk ch at ch * 64 in its row of
   // K / 2 bytes. Prepacked layout: the tile's chunk is one 32 KB run (rows of
   // 64 bytes), so an instruction reads 1 KB of whole lines.
-  const bool packed_layout = p.prepacked != 0;
+  constexpr bool packed_layout = PK;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + wbase * (K / 8)), 0, Nw * (K / 8) * 4, kBufferFlags);
   uint32_t woff[4];
@@ -415,7 +415,9 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 // blocks.
 constexpr int kXcds = 8;
 
-template <int PHASE>
+// PK: the weights are in the prepacked layout (a separate instance, so that
+// traces tell the two apart)
+template <int PHASE, bool PK>
 __global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p) {
   const int n_tiles = p.N / tile_cols<PHASE>();
   const int x = blockIdx.x % kXcds;
@@ -433,10 +435,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p)
     n_valid += __popcll(__ballot(r < kBM && p.sorted_ids[row0 + r] < p.P));
   }
   const int msub = uniform((n_valid + 15) >> 4);
-  if (msub <= 2) block_tile<PHASE, 2>(p, mblk, tile);
-  else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4)>(p, mblk, tile);
-  else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6)>(p, mblk, tile);
-  else block_tile<PHASE, kMaxMS>(p, mblk, tile);
+  if (msub <= 2) block_tile<PHASE, 2, PK>(p, mblk, tile);
+  else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4), PK>(p, mblk, tile);
+  else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6), PK>(p, mblk, tile);
+  else block_tile<PHASE, kMaxMS, PK>(p, mblk, tile);
 }
 
 template <int PHASE>
@@ -452,8 +454,10 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE>),
-                         dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+  const void* fn = p.prepacked
+                       ? reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, true>)
+                       : reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
 }
 
 }  // namespace

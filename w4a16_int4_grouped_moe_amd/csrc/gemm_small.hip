@@ -220,7 +220,7 @@ __device__ __forceinline__ void int4_step(const u32x4 (&w)[NR], const uint8_t* s
 
 // NB blocks of four rows starting at row0 (NB > 1 only for the bf16 shared
 // expert: its weights are then read once for 4 NB tokens).
-template <int PHASE, int NR, bool INT4, int NB, int DEPTH>
+template <int PHASE, int NR, bool INT4, int NB, int DEPTH, bool PK = false>
 __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, int slice0,
                                            uint8_t* lds) {
   static_assert(INT4 ? NB == 1 : NB >= 1, "int4 work items hold one block");
@@ -283,7 +283,7 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
   const int e = INT4 ? p.block_expert[row0 / 4] : 0;
   // prepacked weights (see internal.h): tiles of kPackRows rows, each 128-input
   // chunk of a tile and each 16-group scale period of it one contiguous run
-  const bool packed_layout = INT4 && p.prepacked != 0;
+  constexpr bool packed_layout = INT4 && PK;
   auto stage_scales = [&]() {
     const int64_t r0 = (int64_t)e * Nw;
     const __amdgpu_buffer_rsrc_t sres =
@@ -553,7 +553,9 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 // bytes of a routed one (bf16 weights), so starting them first keeps them out
 // of the kernel's tail. Routed work-groups (one 4-row bucket block each)
 // follow.
-template <int PHASE, int NR, int NRS, int TB>
+// PK: the routed weights are in the prepacked layout (a separate instance, so
+// that traces tell the two apart)
+template <int PHASE, int NR, int NRS, int TB, bool PK>
 __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // small_lds_bytes
   const int64_t bid = blockIdx.x;
@@ -569,7 +571,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kerne
     const int64_t blk = b2 / wg_slices;
     const int s = (int)(b2 - blk * wg_slices);
     if (blk * 4 >= *p.n_padded) return;
-    small_tile<PHASE, NR, true, 1, kSmallDepth>(p, blk * 4, s * kWaves, lds);
+    small_tile<PHASE, NR, true, 1, kSmallDepth, PK>(p, blk * 4, s * kWaves, lds);
   }
 }
 
@@ -599,7 +601,7 @@ int stream_lds_bytes(int K) {
   return niters * kXBytes + 2 * stream_rows<NR>() * scale_row_bytes(K);
 }
 
-template <int NR, int DEPTH>
+template <int NR, int DEPTH, bool PK>
 __device__ __forceinline__ void down_stream_tile(const GemmParams& p, int64_t row0, int sg0,
                                                  int nsg, uint8_t* lds) {
   const int tid = threadIdx.x;
@@ -619,7 +621,7 @@ __device__ __forceinline__ void down_stream_tile(const GemmParams& p, int64_t ro
 
   const int e = p.block_expert[row0 / 4];
   const int64_t r0 = (int64_t)e * p.N;
-  const bool packed_layout = p.prepacked != 0;  // see internal.h
+  constexpr bool packed_layout = PK;  // see internal.h
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + r0 * (K / 8)), 0, p.N * rowbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t sres =
@@ -810,7 +812,7 @@ __device__ __forceinline__ void down_stream_tile(const GemmParams& p, int64_t ro
 
 // Shared-expert work-groups first (as in small_gemm_kernel), then routed ones:
 // each 4-row bucket block is split into runs of `sgs` slice groups.
-template <int NR, int NRS, int TB>
+template <int NR, int NRS, int TB, bool PK>
 __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void stream_down_kernel(GemmParams p,
                                                                                    int sgs) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // stream_down_lds_bytes
@@ -829,7 +831,7 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void stream_down_kern
     const int q = (int)(b2 - blk * runs);
     if (blk * 4 >= *p.n_padded) return;
     const int sg0 = q * sgs;
-    down_stream_tile<NR, kSmallDepth>(p, blk * 4, sg0, min(sgs, groups - sg0), lds);
+    down_stream_tile<NR, kSmallDepth, PK>(p, blk * 4, sg0, min(sgs, groups - sg0), lds);
   }
 }
 
@@ -1153,8 +1155,10 @@ hipError_t launch_small_tb(const GemmParams& p, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS, TB>),
-                         dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
+  const void* fn = p.prepacked
+                       ? reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS, TB, true>)
+                       : reinterpret_cast<const void*>(&small_gemm_kernel<PHASE, NR, NRS, TB, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
 }
 
 // A few tokens: the shared weights are read once per 4 kTokBlocks tokens by
@@ -1192,8 +1196,10 @@ hipError_t launch_stream_down(const GemmParams& p, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
   void* kargs[] = {&args, &sgs};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stream_down_kernel<NR, NRS, TB>),
-                         dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
+  const void* fn = p.prepacked
+                       ? reinterpret_cast<const void*>(&stream_down_kernel<NR, NRS, TB, true>)
+                       : reinterpret_cast<const void*>(&stream_down_kernel<NR, NRS, TB, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, (size_t)lds, stream);
 }
 
 }  // namespace
