@@ -44,11 +44,15 @@
 namespace moe {
 namespace {
 
-// cache policy bits of the int4 weight copies
+// cache policy bits of the int4 weight copies: the default policy in the
+// checkpoint layout (the rest of each line is read a chunk later and should
+// stay in L2), non-temporal in the prepacked layout (every line is used whole
+// by one copy)
 #ifndef MOE_PREFILL_AUX
 #define MOE_PREFILL_AUX 0
 #endif
 constexpr int kPrefillAux = MOE_PREFILL_AUX;
+constexpr int kPrefillPackedAux = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -241,7 +245,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(dst + (4 * wave + i) * 1024), 16,
-                                               woff[i], so, 0, kPrefillAux);
+                                               woff[i], so, 0, PK ? kPrefillPackedAux : kPrefillAux);
   };
 
   // ---- scale copies: instruction v covers rows 32v..32v+31 (32 B each) -------
