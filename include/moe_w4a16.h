@@ -219,10 +219,11 @@ int moe_w4a16_forward_scores(const void *x, const float *scores, int32_t num_sco
  * only moe_w4a16_prepack writes it and only the *_prepacked calls read it).
  * Results are bit for bit those of moe_w4a16_forward on the original weights.
  *
- * Supported widths: hidden % 512 == 0, inter % 256 == 0 and inter > 512
- * (e.g. the full Kimi-K2.6 layer, 7168 / 2048); others give
- * MOE_ERR_UNSUPPORTED (use moe_w4a16_forward). The buffer depends on
- * hidden, inter and num_experts only.
+ * Supported widths: hidden % 512 == 0 and inter % 256 == 0 (e.g. the full
+ * Kimi-K2.6 layer, 7168 / 2048, and one GPU's share of an 8-way tensor-
+ * parallel split, 7168 / 256); others give MOE_ERR_UNSUPPORTED (use
+ * moe_w4a16_forward). The buffer depends on hidden, inter and num_experts
+ * only.
  *
  * moe_w4a16_prepack_size: bytes of the prepacked buffer (host only; about the
  * size of packed_w13 + scales_w13 + packed_w2 + scales_w2).

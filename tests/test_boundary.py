@@ -226,9 +226,12 @@ def test_prepack_sizes_and_supported_widths(lib):
     codes2, scales2 = 3 * 512 * 768 // 2, 3 * 512 * 2 * 32
     assert moe.prepack_size(512, 768, 3) == (rnd(codes13) + rnd(scales13) + rnd(codes2) +
                                              rnd(scales2))
-    # widths the layout does not serve: the narrow down kernel's (inter <= 512),
-    # and widths the prefill tiles do not fit
-    for hidden, inter in ((7168, 256), (7168, 512), (640, 1024), (1024, 640)):
+    # the tensor-parallel share (inter 256, the narrow down kernel) is served;
+    # its W2 rows' 8 scale groups are padded to one period of 16
+    assert moe.prepack_size(7168, 256, 384) == 384 * (2 * 256 * 7168 * 9 // 16 +
+                                                      7168 * 256 // 2 + 7168 * 16 * 2)
+    # widths the prefill tiles do not fit are not
+    for hidden, inter in ((7168, 384), (640, 1024), (1024, 640), (7040, 2048)):
         n = ctypes.c_size_t()
         pp = P(hidden=hidden, inter=inter)
         assert lib.moe_w4a16_prepack_size(ctypes.byref(pp), ctypes.byref(n)) == \
@@ -251,7 +254,7 @@ def test_prepack_argument_errors_before_launch(lib):
     assert call(w, b=None) == moe.MOE_ERR_NULL
     assert call(w, b=ctypes.c_void_p(0x90004)) == moe.MOE_ERR_ALIGNMENT
     assert call(w, n=need - 1) == moe.MOE_ERR_WORKSPACE
-    assert call(w, pp=P(num_experts=4, inter=256)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(w, pp=P(num_experts=4, inter=384)) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_forward_prepacked_argument_errors_before_launch(lib):
@@ -272,6 +275,6 @@ def test_forward_prepacked_argument_errors_before_launch(lib):
     assert call(x=None) == moe.MOE_ERR_NULL
     assert call(out=ctypes.c_void_p(0x10004)) == moe.MOE_ERR_ALIGNMENT
     assert call(wsn=ws - 1) == moe.MOE_ERR_WORKSPACE
-    assert call(pp=P(num_experts=4, inter=256)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(pp=P(num_experts=4, inter=384)) == moe.MOE_ERR_UNSUPPORTED
     # zero tokens: a no-op that touches no pointer
     assert call(b=None, x=None, pp=P(num_tokens=0, num_experts=4)) == moe.MOE_OK

@@ -8,9 +8,9 @@ each 64-row slice; codes [chunk of 128 inputs][row][4 groups x 16 B], scales
 weights does the same arithmetic on the same values as the layer on the
 original weights, so the two outputs must be equal bit for bit; that is
 checked on every kernel path the prepacked form reaches: the small-batch
-kernels (streamed down for inter <= 2048, the general down kernel beyond), and
-prefill blocks with 2, 4 and 6 active sub-tiles; one case is also compared with
-the oracle directly."""
+kernels (the narrow down kernel for inter <= 512, streamed down up to 2048, the
+general down kernel beyond), and prefill blocks with 2, 4 and 6 active
+sub-tiles; one case is also compared with the oracle directly."""
 import numpy as np
 import pytest
 
@@ -95,6 +95,9 @@ CASES = [
     (40, 512, 768, 16, 2, 0, True, 96),    # prefill blocks, ~5 rows per expert (2 sub-tiles)
     (120, 512, 1024, 8, 4, 0, True, 96),   # ~50 rows per expert (4 sub-tiles)
     (300, 1024, 1024, 4, 2, 2, False, 96),  # ~100 rows per expert (6 + 2 sub-tiles), base
+    (6, 1024, 256, 8, 4, 0, True, 4),      # narrow down kernel, K = 256 (two tiles of rows)
+    (9, 512, 512, 8, 3, 1, False, 4),      # narrow down kernel, K = 512, expert base
+    (200, 1024, 256, 8, 4, 0, True, 96),   # prefill blocks with K = 256 for down
 ]
 
 

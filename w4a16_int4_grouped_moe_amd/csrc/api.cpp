@@ -349,12 +349,12 @@ static PackLayout pack_layout(const moe_w4a16_problem* p) {
 }
 
 // Widths the prepacked layout serves: every batch size must run on the
-// small-batch and prefill kernels, which read it (the tiled kernel and the
-// narrow down kernel for inter <= 512 do not).
+// small-batch (with the narrow down kernel) and prefill kernels, which read
+// it; the tiled kernel, used where the prefill tiles do not fit, does not.
 static int check_prepack_problem(const moe_w4a16_problem* p) {
   const int st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (!moe::prefill_fits(p->hidden, p->inter) || p->inter <= 512) return MOE_ERR_UNSUPPORTED;
+  if (!moe::prefill_fits(p->hidden, p->inter)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -873,7 +873,7 @@ constexpr int narrow_rows() { return 4 * NR * (16 / KG); }
 // NB blocks of four rows (routed: one 4-row bucket block; shared: NB blocks of
 // consecutive tokens) against the weight rows of kNarrowSteps wave steps from
 // n0 (fewer where N ends first: a wave takes the steps that start below N).
-template <int KG, int NR, bool INT4, int NB, int DEPTH>
+template <int KG, int NR, bool INT4, int NB, int DEPTH, bool PK = false>
 __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, int n0) {
   constexpr int RC = 16 / KG;
   constexpr int RW = narrow_rows<KG, NR>();
@@ -915,12 +915,21 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
   const int Nw = p.N;
   const int e = INT4 ? p.block_expert[row0 / 4] : 0;
   const int64_t r0 = (int64_t)e * Nw;
+  // prepacked weights (see internal.h): a step's kWaves * RW rows lie in one
+  // tile (the work-group's first row is a multiple of kPackRows), so a lane's
+  // offset is its place in the step's rows plus the step's uniform base
+  constexpr bool packed_layout = INT4 && PK;
   __amdgpu_buffer_rsrc_t wres, sres;
   if (INT4) {
     wres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.packed + r0 * (K / 8)), 0,
                                              Nw * (K / 8) * 4, kBufferFlags);
-    sres = __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
-                                             Nw * (K / 32) * 2, kBufferFlags);
+    sres = packed_layout
+               ? __builtin_amdgcn_make_buffer_rsrc(
+                     (void*)(reinterpret_cast<const uint8_t*>(p.scales) +
+                             e * pack_scale_bytes(Nw, K)),
+                     0, (int)pack_scale_bytes(Nw, K), kBufferFlags)
+               : __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + r0 * (K / 32)), 0,
+                                                   Nw * (K / 32) * 2, kBufferFlags);
   } else {
     wres = __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
     sres = wres;
@@ -928,18 +937,33 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
   auto row_of = [&](int step, int rs) {
     return n0 + (step * kWaves + wave) * RW + 4 * (rs * RC + c) + j;
   };
+  static_assert(kPackRows % (kWaves * RW) == 0, "narrow steps inside prepacked tiles");
   int woff[NR], soff[NR];
 #pragma unroll
   for (int rs = 0; rs < NR; ++rs) {
     const int row = row_of(0, rs);
-    woff[rs] = !gvalid ? kOutOfRange : INT4 ? (row * (K / 8) + 4 * g) * 4 : (row * K + 32 * g) * 2;
-    soff[rs] = gvalid ? (row * (K / 32) + g) * 2 : kOutOfRange;
+    const int lr = row - n0;  // row inside the step
+    if (packed_layout) {
+      woff[rs] = gvalid ? (int)pack_code_offset(false, 0, K, lr, g) : kOutOfRange;
+      soff[rs] = gvalid ? (int)pack_scale_offset(false, 0, K, lr, g) : kOutOfRange;
+    } else {
+      woff[rs] = !gvalid ? kOutOfRange : INT4 ? (row * (K / 8) + 4 * g) * 4 : (row * K + 32 * g) * 2;
+      soff[rs] = gvalid ? (row * (K / 32) + g) * 2 : kOutOfRange;
+    }
   }
   const int wstep = kWaves * RW * (INT4 ? K / 2 : 2 * K);  // bytes per step
   const int sstep = kWaves * RW * (K / 32) * 2;
   auto sofs = [&](int step, int bytes) {
     return uniform(step < nsteps ? step * bytes : kOutOfRange);
   };
+  // prepacked: the uniform base of step `step` (its first row's tile and row)
+  auto pofs = [&](int step, int tile_bytes, int row_bytes) {
+    const int rb = n0 + step * kWaves * RW;
+    return uniform(step < nsteps
+                       ? (rb / kPackRows) * tile_bytes + (rb % kPackRows) * row_bytes
+                       : kOutOfRange);
+  };
+  const int ptile_w = pack_chunks(K) * kPackRows * 64, ptile_s = pack_periods(K) * kPackRows * 32;
 
   struct Frag {
     u32x4 w[NR][INT4 ? 1 : 4];
@@ -949,9 +973,12 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
 #pragma unroll
     for (int rs = 0; rs < NR; ++rs) {
       if (INT4) {
-        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(wres, woff[rs], sofs(step, wstep),
-                                                           kStreamAux);
-        f.s[rs] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff[rs], sofs(step, sstep), kScaleAux);
+        f.w[rs][0] = __builtin_amdgcn_raw_buffer_load_b128(
+            wres, woff[rs], packed_layout ? pofs(step, ptile_w, 64) : sofs(step, wstep),
+            kStreamAux);
+        f.s[rs] = __builtin_amdgcn_raw_buffer_load_b16(
+            sres, soff[rs], packed_layout ? pofs(step, ptile_s, 32) : sofs(step, sstep),
+            kScaleAux);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -1077,10 +1104,10 @@ __device__ __forceinline__ void narrow_tile(const GemmParams& p, int64_t row0, i
 // Work-groups: shared-expert items first (kTokBlocks 4-token blocks each),
 // then routed 4-row bucket blocks; each takes kNarrowSteps wave steps of
 // consecutive weight rows.
-template <int KG, int NR, int NRS>
 #ifndef MOE_NARROW_WAVES
 #define MOE_NARROW_WAVES 3
 #endif
+template <int KG, int NR, int NRS, bool PK>
 __global__ __launch_bounds__(kThreads, MOE_NARROW_WAVES) void narrow_down_kernel(GemmParams p) {
   const int64_t bid = blockIdx.x;
   constexpr int kRowsWGs = kNarrowSteps * kWaves * narrow_rows<KG, NRS>();
@@ -1097,7 +1124,7 @@ __global__ __launch_bounds__(kThreads, MOE_NARROW_WAVES) void narrow_down_kernel
     const int64_t blk = b2 / cr;
     const int n0 = (int)(b2 - blk * cr) * kRowsWG;
     if (blk * 4 >= *p.n_padded) return;
-    narrow_tile<KG, NR, true, 1, kNarrowDepth>(p, blk * 4, n0);
+    narrow_tile<KG, NR, true, 1, kNarrowDepth, PK>(p, blk * 4, n0);
   }
 }
 
@@ -1125,8 +1152,10 @@ hipError_t launch_narrow(const GemmParams& p, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&narrow_down_kernel<KG, NR, NRS>),
-                         dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+  const void* fn = p.prepacked
+                       ? reinterpret_cast<const void*>(&narrow_down_kernel<KG, NR, NRS, true>)
+                       : reinterpret_cast<const void*>(&narrow_down_kernel<KG, NR, NRS, false>);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
 }
 
 // Dynamic LDS of a launch: two activation stages (of the larger of the routed
