@@ -152,3 +152,40 @@ def test_prepacked_zero_tokens(dev):
     w = torch.empty((0, 2), dtype=torch.float32, device=dev)
     out = moe.forward_prepacked(x, ids, w, pk)
     assert out.shape == (0, 512)
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(6, 1024, 768, 8, 2), (150, 1024, 768, 8, 4)])
+def test_prepacked_graph_capture_replay(dev, T, H, I, E, k):
+    """A captured prepacked forward (small-batch kernels; prefill blocks with
+    the shared expert in the library GEMM, whose handle the eager call creates
+    first) replays to the eager result, with eager work between replays."""
+    import torch
+    import w4a16_int4_grouped_moe_amd as moe
+
+    bank = mi.weight_bank(31 + T, H, I, list(range(E)))
+    bd = device_bank(bank, dev)
+    pk = moe.prepack(bd["packed_w13"], bd["scales_w13"], bd["packed_w2"], bd["scales_w2"])
+    d = lambda a: mi.to_device(a, dev)
+    ids, w = mi.routing_uniform(32 + T, T, E, k)
+    xs, ids_d, w_d = d(mi.activations(33 + T, T, H)), d(ids), d(w)
+    sw = d(mi.shared_weights(34 + T, H, I))
+    p = moe.problem(T, H, I, E, k)
+    ws = torch.empty(moe.workspace_size(p), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    eager = moe.forward_prepacked(xs, ids_d, w_d, pk, sw, workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward_prepacked(xs, ids_d, w_d, pk, sw, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward_prepacked(xs, ids_d, w_d, pk, sw, out=out, workspace=ws)
+    for i in range(4):
+        out.zero_()
+        ws.fill_(0xFF)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        moe.forward_prepacked(xs[:5], ids_d[:5], w_d[:5], pk, sw)
+        torch.cuda.synchronize()
