@@ -317,7 +317,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int mblk, int til
 // range of items was measured slower on MI355X than the default round-robin
 // placement, for this kernel and for the small-batch one.)
 template <int BM, int PHASE, int NSUB, int NSUBS>
-__global__ __launch_bounds__(kThreads, BM >= 128 ? 2 : 1) void grouped_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLdsRow];
   const int n_tiles = p.N / tile_cols<PHASE, NSUB>();
   const int routed = p.max_blocks * n_tiles;
@@ -354,19 +354,17 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// 16 and 64-row blocks: 2 column sub-tiles per wave; 128-row blocks: 4, so that
-// each LDS activation read feeds more MFMAs.
+// 16- and 64-row blocks (the sizes the layer call picks for this kernel), two
+// column sub-tiles per wave.
 hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stream) {
   if (block_m == 16) return launch<16, kGateUp, 2, 2>(p, stream);
   if (block_m == 64) return launch<64, kGateUp, 2, 2>(p, stream);
-  if (block_m == 128) return launch<128, kGateUp, 4, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_down(const GemmParams& p, int32_t block_m, hipStream_t stream) {
   if (block_m == 16) return launch<16, kDown, 2, 2>(p, stream);
   if (block_m == 64) return launch<64, kDown, 2, 2>(p, stream);
-  if (block_m == 128) return launch<128, kDown, 4, 2>(p, stream);
   return hipErrorInvalidValue;
 }
 

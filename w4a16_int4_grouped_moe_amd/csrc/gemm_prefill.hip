@@ -1,8 +1,8 @@
 // gemm_prefill.hip -- grouped W4A16 GEMMs for many rows per expert (gfx950):
-// the int4 routed experts of prefill-sized batches, 128-row bucket blocks.
+// the int4 routed experts of prefill-sized batches, 96-row bucket blocks.
 //
 // Same two launches as the other GEMM paths (gate_up with the SwiGLU epilogue,
-// then down), for blocks of 128 bucketed rows of one expert. Here the layer is
+// then down), for blocks of 96 bucketed rows of one expert. Here the layer is
 // a dense contraction per expert (about 85 rows each for 4096 tokens, top-8 of
 // 384), so the kernel is built around keeping the MFMA pipes fed: every
 // dequantised weight serves all rows of the block, and all operands arrive

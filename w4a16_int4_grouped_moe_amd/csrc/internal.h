@@ -111,7 +111,7 @@ bool small_batch_fits(int32_t hidden, int32_t inter);
 hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_small(const GemmParams& p, hipStream_t stream);
 
-// Routed int4 experts in 128-row blocks (prefill-sized batches; see
+// Routed int4 experts in 96-row blocks (prefill-sized batches; see
 // gemm_prefill.hip). prefill_fits: whether the widths suit its tiles.
 bool prefill_fits(int32_t hidden, int32_t inter);
 int32_t prefill_block_m();  // bucket rows per block of that path
