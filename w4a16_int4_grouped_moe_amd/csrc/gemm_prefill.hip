@@ -33,8 +33,8 @@
 //    lane, so its 32-long reduction covers one 8-input slice of each of the
 //    four groups; the matching activations are read at those offsets. The
 //    next step's dequantisation (VALU) is interleaved with this step's MFMAs.
-// One barrier per chunk: the copies of chunk c + 1 are issued before chunk c is
-// computed and waited for after it. Barriers are raw s_barrier with explicit
+// One barrier per chunk: the copies of chunk c + 1 are issued during the first
+// MFMA step of chunk c and waited for after it. Barriers are raw s_barrier with explicit
 // waits (the fence of __syncthreads() would also wait for the copies just
 // issued). The number of 16-row sub-tiles holding bucket rows (even, after
 // rounding up) is a template parameter of the K loop, so the loop body is
@@ -287,6 +287,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   }
   // scales: row R, group 4 (chunk % 4) + lq
   const int sread = (wave * 64 + lr) * kSRowBytes + lq * 2;
+  constexpr int kMaxCopies = kAPerWave + 4 + 2;  // copy instructions per wave and chunk
   // activations: row 16 mi + lr, piece 4 lq + j (permuted slot)
   const int aread = lr * (kKC * 2);
 
@@ -296,7 +297,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const float (&sc)[kNSub]) {
+  // issue_copies() is called in the first MFMA step; the scheduler spreads its
+  // copy instructions between that step's MFMAs.
+  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const float (&sc)[kNSub],
+                     auto&& issue_copies) {
     GroupScale gs[kNSub];
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) gs[s] = group_scale(sc[s]);
@@ -320,13 +324,16 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
         for (int s = 0; s < kNSub; ++s)
           acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], bw[j & 1][s], acc[mi][s], 0, 0, 0);
+      if (j == 0) issue_copies();
       // interleave: the activation reads first, then one MFMA per three VALU
-      // instructions of the next step's dequantisation
+      // instructions of the next step's dequantisation, and in the first step
+      // one copy after each of the first MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
 #pragma unroll
       for (int i = 0; i < MS * kNSub; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        if (j == 0 && i < kMaxCopies) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -341,9 +348,11 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 
   // The chunk's scales and this wave's weight words are read from LDS first;
   // the weight buffer is then free (each wave copies and reads only its own
-  // rows), so the copy of chunk ch + 2 goes into it at once: weights are
+  // rows), so the copy of chunk ch + 2 goes into it in this chunk: weights are
   // fetched two chunks ahead, activations (shared by all waves, buffer freed
-  // by the barrier) one chunk ahead.
+  // by the barrier) one chunk ahead. The copies are issued between the first
+  // step's MFMAs, not as one burst after the barrier: a burst from all eight
+  // waves at once stalls them on issue with no MFMA work in flight.
   auto chunk = [&](int ch, uint8_t* abuf, uint8_t* anext, uint8_t* wbuf) {
     float sc[kNSub];
     read_scales(sc, ch);
@@ -352,12 +361,12 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     for (int s = 0; s < kNSub; ++s) w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread[s]);
     wait_lgkm0();
     __builtin_amdgcn_sched_barrier(0);
-    copy_a(anext, ch + 1);
-    copy_w(wbuf, ch + 2);
     const bool new_s = ch % kSPeriod == 0 && ch / kSPeriod + 1 < nper;
-    if (new_s) copy_s(((ch / kSPeriod + 1) & 1) ? lds_s1 : lds_s0, ch / kSPeriod + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(abuf, w, sc);
+    compute(abuf, w, sc, [&]() {
+      copy_a(anext, ch + 1);
+      copy_w(wbuf, ch + 2);
+      if (new_s) copy_s(((ch / kSPeriod + 1) & 1) ? lds_s1 : lds_s0, ch / kSPeriod + 1);
+    });
     // activations and weights of chunk ch + 1 in LDS (the copies of chunk
     // ch + 2's weights and of the next scales may stay in flight); this
     // chunk's LDS reads done before its activation buffer is overwritten
