@@ -552,15 +552,38 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
 // tokens reads the shared weights once) come first: each streams twice the
 // bytes of a routed one (bf16 weights), so starting them first keeps them out
 // of the kernel's tail. Routed work-groups (one 4-row bucket block each)
-// follow.
+// follow. In small grids the shared work-groups are moved (place_shared).
 // PK: the routed weights are in the prepacked layout (a separate instance, so
 // that traces tell the two apart)
+// Where the shared expert's work-groups sit in the grid. Work-groups go to the
+// 8 XCDs in id order, round-robin, and within an XCD to its 32 CUs in turn, so
+// id i lands on CU slot (i / 8) % 32 of XCD i % 8, and each run of 256 ids puts
+// one work-group on every CU. A small grid (at most three work-groups per CU,
+// all resident at once) gives the CU slots below (G % 256) / 8 one work-group
+// more than the others; the shared expert's work-groups, which stream about
+// twice the bytes of a routed one, are then placed at ids [G % 256, G % 256 +
+// shared) of the first run, which reach the other CU slots. A CU streams at a
+// bounded rate, so the launch lasts as long as its most loaded CU: for one
+// token (128 shared and 512 routed work-groups) the most loaded CUs carry 717
+// or 774 KB instead of 975 KB. Larger grids keep the shared work-groups first,
+// out of the kernel's tail (and grids below one work-group per CU need no
+// placement). The result is a permutation of work-group ids.
+constexpr int64_t kChipCUs = 256;
+__device__ __forceinline__ int64_t place_shared(int64_t bid, int64_t shared) {
+  const int64_t grid = gridDim.x;
+  const int64_t s0 = grid % kChipCUs;
+  if (grid < kChipCUs || grid > 3 * kChipCUs || s0 + shared > kChipCUs) return bid;
+  if (bid < s0) return bid + shared;      // routed work-groups before them
+  if (bid < s0 + shared) return bid - s0;  // the shared expert's
+  return bid;                              // routed work-groups after them
+}
+
 template <int PHASE, int NR, int NRS, int TB, bool PK>
 __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // small_lds_bytes
-  const int64_t bid = blockIdx.x;
   const int ns = p.N / slice_cols<PHASE, NRS>() / kWaves;
   const int64_t shared = p.wshared ? (p.T + 4 * TB - 1) / (4 * TB) * ns : 0;
+  const int64_t bid = place_shared(blockIdx.x, shared);
   if (bid < shared) {
     const int64_t tg = bid / ns;
     const int s = (int)(bid - tg * ns);
