@@ -167,3 +167,26 @@ def test_tp8_share_prefill_sampled(dev, tp8):
     print(f"[case] tp8_prefill block_m "
           f"{moe.forward_block_m(moe.problem(4096, g.hidden, g.inter, 384, 8, 0))}", flush=True)
     _kimi_case(dev, tp8, "tp8_prefill", 4096, n_sample=12)
+
+
+def test_tp8_share_prefill_prepacked_bit_exact(dev, tp8):
+    """One GPU's share (intermediate 256) at 4096 tokens. Its down projection
+    is two 128-input chunks per column tile, so each work-group of the down
+    launch takes several consecutive tiles (four here: ~420 real blocks of 14
+    tiles) with one copy stream across them. The layer on prepacked weights
+    takes the same path and must equal the checkpoint-layout layer bit for
+    bit (the sampled rows above are checked against the oracle)."""
+    import torch
+    import w4a16_int4_grouped_moe_amd as moe
+
+    bank, shared = tp8
+    w = mi.workload("tp8_prefill", 4096)
+    x = mi.activations(w.seed_x + w.T, w.T, w.geo.hidden)
+    ids, wts = mi.make_routing(w)
+    print("[case] tp8_prefill T=4096 prepacked vs checkpoint layout", flush=True)
+    ref = run_layer(dev, x, ids, wts, bank, shared)
+    pk = moe.prepack(bank["packed_w13"], bank["scales_w13"], bank["packed_w2"], bank["scales_w2"])
+    d = lambda a: mi.to_device(a, dev)
+    got = moe.forward_prepacked(d(x), d(ids), d(wts), pk, d(shared))
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))

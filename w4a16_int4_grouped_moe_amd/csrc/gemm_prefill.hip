@@ -176,8 +176,11 @@ __device__ __forceinline__ int weight_row(const GemmParams& p, int tile, int R) 
   return tile * kBN + w * 64 + 16 * s + r;
 }
 
-template <int PHASE, int MS, bool PK>
-__device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int tile) {
+// MT: the work-group computes ntl consecutive column tiles of the block
+// (otherwise exactly one: ntl is then the constant 1)
+template <int PHASE, int MS, bool PK, bool MT>
+__device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int tile, int ntl_arg) {
+  const int ntl = MT ? ntl_arg : 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -213,8 +216,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     }
     aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
   }
-  auto copy_a = [&](uint8_t* dst, int ch) {
-    const int so = uniform(ch < nch ? ch * kKC * 2 : (int)kNoRow);
+  // copies are addressed by (tile t of the work-group's tiles, chunk c of it);
+  // past the last tile an offset beyond any buffer (loads zeros)
+  auto copy_a = [&](uint8_t* dst, int t, int c) {
+    const int so = uniform(t < ntl ? c * kKC * 2 : (int)kNoRow);
 #pragma unroll
     for (int i = 0; i < kAPerWave; ++i) {
       const int t = kAPerWave * wave + i;
@@ -240,8 +245,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
                   : (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 8) + 4 * g) * 4);
   }
   const int wstep = packed_layout ? kWBytes : kWRowBytes;  // bytes per chunk
-  auto copy_w = [&](uint8_t* dst, int ch) {
-    const int so = uniform(ch < nch ? ch * wstep : (int)kNoRow);
+  // bytes from one tile's weights to the next tile's
+  const int wtile = packed_layout ? nch * kWBytes : tile_cols<PHASE>() * (K / 2);
+  auto copy_w = [&](uint8_t* dst, int t, int c) {
+    const int so = uniform(t < ntl ? t * wtile + c * wstep : (int)kNoRow);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(dst + (4 * wave + i) * 1024), 16,
@@ -269,8 +276,9 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
                   : (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 32) + 8 * (lane & 1)) * 2);
   }
   const int sstep = packed_layout ? kSBytes : kSRowBytes;  // bytes per period
-  auto copy_s = [&](uint8_t* dst, int per) {
-    const int so = uniform(per < nper ? per * sstep : (int)kNoRow);
+  const int stile = packed_layout ? nper * kSBytes : tile_cols<PHASE>() * (K / 16);
+  auto copy_s = [&](uint8_t* dst, int t, int lp) {
+    const int so = uniform(t < ntl ? t * stile + lp * sstep : (int)kNoRow);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_ptr)(dst + (2 * wave + i) * 1024), 16,
@@ -338,9 +346,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_scales = [&](float (&sc)[kNSub], int ch) {
-    const uint8_t* sb = ((ch / kSPeriod) & 1) ? lds_s1 : lds_s0;
-    const int g = (ch % kSPeriod) * 8;  // bytes: 4 groups per chunk
+  auto read_scales = [&](float (&sc)[kNSub], int t, int c) {
+    const int per = t * nper + c / kSPeriod;  // period count across the tiles
+    const uint8_t* sb = (per & 1) ? lds_s1 : lds_s0;
+    const int g = (c % kSPeriod) * 8;  // bytes: 4 groups per chunk
 #pragma unroll
     for (int s = 0; s < kNSub; ++s)
       sc[s] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sb + sread + s * 16 * kSRowBytes + g));
@@ -353,19 +362,27 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // by the barrier) one chunk ahead. The copies are issued between the first
   // step's MFMAs, not as one burst after the barrier: a burst from all eight
   // waves at once stalls them on issue with no MFMA work in flight.
-  auto chunk = [&](int ch, uint8_t* abuf, uint8_t* anext, uint8_t* wbuf) {
+  auto chunk = [&](int t, int c, uint8_t* abuf, uint8_t* anext, uint8_t* wbuf) {
     float sc[kNSub];
-    read_scales(sc, ch);
+    read_scales(sc, t, c);
     u32x4 w[kNSub];
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread[s]);
     wait_lgkm0();
     __builtin_amdgcn_sched_barrier(0);
-    const bool new_s = ch % kSPeriod == 0 && ch / kSPeriod + 1 < nper;
+    // the chunk after this one and the one after that (nch is even, so a
+    // tile boundary falls between two chunks of a pair)
+    const int t1 = c + 1 < nch ? t : t + 1, c1 = c + 1 < nch ? c + 1 : 0;
+    const int t2 = c + 2 < nch ? t : t + 1, c2 = c + 2 < nch ? c + 2 : c + 2 - nch;
+    // the next scale period, at the first chunk of each period
+    const int lp = c / kSPeriod;
+    const int tn = lp + 1 < nper ? t : t + 1, lpn = lp + 1 < nper ? lp + 1 : 0;
+    const bool new_s = c % kSPeriod == 0 && tn < ntl;
+    const int pbuf = (t * nper + lp + 1) & 1;
     compute(abuf, w, sc, [&]() {
-      copy_a(anext, ch + 1);
-      copy_w(wbuf, ch + 2);
-      if (new_s) copy_s(((ch / kSPeriod + 1) & 1) ? lds_s1 : lds_s0, ch / kSPeriod + 1);
+      copy_a(anext, t1, c1);
+      copy_w(wbuf, t2, c2);
+      if (new_s) copy_s(pbuf ? lds_s1 : lds_s0, tn, lpn);
     });
     // activations and weights of chunk ch + 1 in LDS (the copies of chunk
     // ch + 2's weights and of the next scales may stay in flight); this
@@ -377,45 +394,65 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   };
 
   // ---- pipeline -----------------------------------------------------------
-  copy_w(lds_w0, 0);
-  copy_w(lds_w1, 1);
-  copy_a(lds_a0, 0);
-  copy_s(lds_s0, 0);
+  copy_w(lds_w0, 0, 0);
+  copy_w(lds_w1, 0, 1);
+  copy_a(lds_a0, 0, 0);
+  copy_s(lds_s0, 0, 0);
   wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  // whole pairs (the chunk count is even; a loop with a second exit between
-  // the halves makes the register allocator move the accumulators)
-  for (int ch = 0; ch < nch; ch += 2) {
-    chunk(ch, lds_a0, lds_a1, lds_w0);
-    chunk(ch + 1, lds_a1, lds_a0, lds_w1);
-  }
-
   // ---- epilogue: lane holds rows 4 lq + i of each 16-row sub-tile, column lr
-  if (PHASE == kGateUp) {
+  auto epilogue = [&](int ctile) {
+    if (PHASE == kGateUp) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int col = tile * (kBN / 2) + wave * 32 + 16 * s + lr;
+      for (int s = 0; s < 2; ++s) {
+        const int col = ctile * (kBN / 2) + wave * 32 + 16 * s + lr;
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t r = row0 + mi * 16 + 4 * lq + i;
+            const float hv = silu_mul(acc[mi][s][i], acc[mi][s + 2][i]);
+            p.h_routed[r * p.I + col] = (uint16_t)(pack_bf16x2(hv, 0.f) & 0xFFFFu);
+          }
+      }
+    } else {
 #pragma unroll
       for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t r = row0 + mi * 16 + 4 * lq + i;
-          const float hv = silu_mul(acc[mi][s][i], acc[mi][s + 2][i]);
-          p.h_routed[r * p.I + col] = (uint16_t)(pack_bf16x2(hv, 0.f) & 0xFFFFu);
+          const int32_t pair = p.sorted_ids[r];
+          if (pair >= p.P) continue;
+          float* dst = p.y_routed + (int64_t)pair * p.N + ctile * kBN + wave * 64 + lr;
+#pragma unroll
+          for (int s = 0; s < kNSub; ++s) dst[16 * s] = acc[mi][s][i];
         }
     }
-  } else {
+  };
+
+  // whole pairs (the chunk count is even; a loop with a second exit between
+  // the halves makes the register allocator move the accumulators)
+  if (!MT) {
+    for (int c = 0; c < nch; c += 2) {
+      chunk(0, c, lds_a0, lds_a1, lds_w0);
+      chunk(0, c + 1, lds_a1, lds_a0, lds_w1);
+    }
+    epilogue(tile);
+    return;
+  }
+  // several tiles: they follow each other without a break in the copy
+  // stream (the last chunks of a tile already fetch the next tile's first
+  // ones); the accumulators restart at zero for each tile
+  for (int t = 0; t < ntl; ++t) {
+    for (int c = 0; c < nch; c += 2) {
+      chunk(t, c, lds_a0, lds_a1, lds_w0);
+      chunk(t, c + 1, lds_a1, lds_a0, lds_w1);
+    }
+    epilogue(tile + t);
 #pragma unroll
     for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = row0 + mi * 16 + 4 * lq + i;
-        const int32_t pair = p.sorted_ids[r];
-        if (pair >= p.P) continue;
-        float* dst = p.y_routed + (int64_t)pair * p.N + tile * kBN + wave * 64 + lr;
-#pragma unroll
-        for (int s = 0; s < kNSub; ++s) dst[16 * s] = acc[mi][s][i];
-      }
+      for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -428,16 +465,9 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 // blocks.
 constexpr int kXcds = 8;
 
-// PK: the weights are in the prepacked layout (a separate instance, so that
-// traces tell the two apart)
-template <int PHASE, bool PK>
-__global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p) {
-  const int n_tiles = p.N / tile_cols<PHASE>();
-  const int x = blockIdx.x % kXcds;
-  const int sx = blockIdx.x / kXcds;
-  const int mblk = (sx / n_tiles) * kXcds + x;
-  const int tile = sx - (sx / n_tiles) * n_tiles;
-  if (mblk >= p.max_blocks || (int64_t)mblk * kBM >= *p.n_padded) return;
+// The block's rows, rounded up to whole 16-row sub-tiles, select the K loop.
+template <int PHASE, bool PK, bool MT>
+__device__ __forceinline__ void run_block(const GemmParams& p, int mblk, int tile, int ntl) {
   // bucket rows of the block (padding sits at its end), in 16-row sub-tiles
   const int64_t row0 = (int64_t)mblk * kBM;
   const int lane = threadIdx.x & 63;
@@ -448,10 +478,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p)
     n_valid += __popcll(__ballot(r < kBM && p.sorted_ids[row0 + r] < p.P));
   }
   const int msub = uniform((n_valid + 15) >> 4);
-  if (msub <= 2) block_tile<PHASE, 2, PK>(p, mblk, tile);
-  else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4), PK>(p, mblk, tile);
-  else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6), PK>(p, mblk, tile);
-  else block_tile<PHASE, kMaxMS, PK>(p, mblk, tile);
+  if (msub <= 2) block_tile<PHASE, 2, PK, MT>(p, mblk, tile, ntl);
+  else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4), PK, MT>(p, mblk, tile, ntl);
+  else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6), PK, MT>(p, mblk, tile, ntl);
+  else block_tile<PHASE, kMaxMS, PK, MT>(p, mblk, tile, ntl);
+}
+
+// One work-group per (block, column tile). PK: the weights are in the
+// prepacked layout (a separate instance, so that traces tell the two apart).
+template <int PHASE, bool PK>
+__global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p) {
+  const int n_tiles = p.N / tile_cols<PHASE>();
+  const int x = blockIdx.x % kXcds;
+  const int sx = blockIdx.x / kXcds;
+  const int mblk = (sx / n_tiles) * kXcds + x;
+  const int tile = sx - (sx / n_tiles) * n_tiles;
+  if (mblk >= p.max_blocks || (int64_t)mblk * kBM >= *p.n_padded) return;
+  run_block<PHASE, PK, false>(p, mblk, tile, 1);
+}
+
+// Short K (a few chunks per tile, e.g. the down projection of one GPU's share
+// of a tensor-parallel layer): a work-group takes up to tpw_max consecutive
+// column tiles of its block, and its copy stream runs on from one tile into
+// the next, so that each tile no longer starts with an empty pipeline and
+// ends with its stores alone. The grid holds one work-group per (block, tile);
+// the tiles per work-group are chosen from the real block count (the grid's
+// is an upper bound), as many as still leave six work-groups per CU, and the
+// work-groups past the last group exit at once.
+template <int PHASE, bool PK>
+__global__ __launch_bounds__(kThreads, 1) void prefill_tiles_kernel(GemmParams p, int tpw_max) {
+  const int n_tiles = p.N / tile_cols<PHASE>();
+  const int64_t nblk = *p.n_padded / kBM;
+  int tpw = 1;
+  for (int c = tpw_max; c > 1; c >>= 1)
+    if (nblk * ((n_tiles + c - 1) / c) >= 6 * 256) {
+      tpw = c;
+      break;
+    }
+  const int ngrp = (n_tiles + tpw - 1) / tpw;  // groups of tpw consecutive tiles
+  const int x = blockIdx.x % kXcds;
+  const int sx = blockIdx.x / kXcds;
+  const int mblk = (sx / ngrp) * kXcds + x;
+  const int tile = (sx - (sx / ngrp) * ngrp) * tpw;
+  if (mblk >= p.max_blocks || (int64_t)mblk * kBM >= *p.n_padded) return;
+  run_block<PHASE, PK, true>(p, mblk, tile, min(tpw, n_tiles - tile));
 }
 
 template <int PHASE>
@@ -462,14 +532,27 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
   const int64_t nw = PHASE == kGateUp ? 2 * (int64_t)p.I : p.N;
   if (arows * p.K * 2 > 0x7fffffff || nw * p.K / 2 > 0x7fffffff) return hipErrorInvalidValue;
   const int64_t blocks = ((int64_t)p.max_blocks + kXcds - 1) / kXcds * kXcds;
-  const int64_t grid = blocks * (p.N / tile_cols<PHASE>());
+  const int n_tiles = p.N / tile_cols<PHASE>();
+  const int nch = p.K / kKC;
+  // several tiles per work-group only where a tile is a few chunks long
+  // (at most 16 chunks per work-group, at most four tiles)
+  int tpw = 1;
+  while (2 * tpw * nch <= 16 && 2 * tpw <= 4) tpw *= 2;
+  const int64_t grid = blocks * n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
-  void* kargs[] = {&args};
+  if (tpw == 1) {
+    void* kargs[] = {&args};
+    const void* fn = p.prepacked
+                         ? reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, true>)
+                         : reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, false>);
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+  }
+  void* kargs[] = {&args, &tpw};
   const void* fn = p.prepacked
-                       ? reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, true>)
-                       : reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, false>);
+                       ? reinterpret_cast<const void*>(&prefill_tiles_kernel<PHASE, true>)
+                       : reinterpret_cast<const void*>(&prefill_tiles_kernel<PHASE, false>);
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
 }
 
