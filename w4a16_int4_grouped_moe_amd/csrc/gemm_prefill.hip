@@ -9,7 +9,8 @@
 // through LDS without holding registers while in flight.
 //
 // Work-group (512 threads = 8 waves): one block of up to kBM bucketed rows x
-// 512 weight rows. Every wave owns four 16-row weight sub-tiles (gate_up: two
+// 512 weight rows (a column tile; where K is only a few chunks, several
+// consecutive tiles of the block in turn, prefill_tiles_kernel). Every wave owns four 16-row weight sub-tiles (gate_up: two
 // gate sub-tiles and the two matching up sub-tiles) and computes them for all
 // of the block's rows, so each weight is dequantised exactly once per block.
 // K advances in chunks of 128 inputs (four 32-input groups). All operands reach
