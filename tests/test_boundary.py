@@ -72,9 +72,10 @@ def test_workspace_size_and_block_m(lib):
     assert moe.forward_block_m(P(num_tokens=193)) == 96
     assert moe.forward_block_m(P(num_tokens=512)) == 96
     assert moe.forward_block_m(P(num_tokens=4096)) == 96
-    # widths the prefill kernel's tiles do not fit (7040 % 512 != 0)
-    assert moe.forward_block_m(P(num_tokens=512, hidden=7040)) == 16
-    assert moe.forward_block_m(P(num_tokens=4096, hidden=7040)) == 64
+    # widths that are not whole block tiles (7040 % 512 != 0, 1152 % 256 != 0)
+    # take the same 96-row blocks, masked
+    assert moe.forward_block_m(P(num_tokens=512, hidden=7040)) == 96
+    assert moe.forward_block_m(P(num_tokens=4096, hidden=7040, inter=1152)) == 96
     # one GPU's share of an 8-way tensor-parallel split (intermediate 256)
     assert moe.forward_block_m(P(inter=256)) == 4
     assert moe.forward_block_m(P(inter=256, num_tokens=4096)) == 96
@@ -110,6 +111,28 @@ def test_invalid_problem_rejected(lib, kw, status):
     fake = ctypes.c_void_p(0x10000)
     args = [fake] * 9
     assert lib.moe_w4a16_forward(*args, ctypes.byref(p), fake, 1 << 40, None) == status
+
+
+@pytest.mark.parametrize("T,status", [
+    (60000, moe.MOE_OK),                 # bucketed h rows: 516,480 x 2048 x 2 B < 2 GiB
+    (70000, moe.MOE_ERR_UNSUPPORTED),    # h rows past 2 GiB
+    (150000, moe.MOE_ERR_UNSUPPORTED),   # x past 2 GiB as well
+])
+def test_arrays_past_2gib_rejected(lib, T, status):
+    """The kernels address every array through 32-bit buffer resources whose
+    out-of-range offset (2^31) must lie past the array: a problem that would
+    need a larger array is refused before any launch."""
+    p = P(num_tokens=T)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_w4a16_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    if status != moe.MOE_OK:
+        fake = ctypes.c_void_p(0x10000)
+        assert lib.moe_w4a16_forward(*([fake] * 9), ctypes.byref(p), fake, 1 << 45,
+                                     None) == status
+    # a shared-expert or expert matrix past 2 GiB (2I x H bf16)
+    p = P(num_tokens=1, hidden=16384, inter=32768)
+    assert lib.moe_w4a16_workspace_size(ctypes.byref(p), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
 
 
 def _fwd(lib, p, ptrs, ws_bytes=1 << 40):

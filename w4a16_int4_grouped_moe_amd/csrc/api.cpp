@@ -22,6 +22,14 @@ static_assert(moe::kMaxExperts == MOE_MAX_EXPERTS,
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+int32_t choose_block_m(const moe_w4a16_problem* p);
+int64_t sorted_capacity(const moe_w4a16_problem* p, int32_t bm);
+
+// Buffer resources of the kernels hold 32-bit byte sizes, and their
+// out-of-range offsets (2^31) must lie past every buffer: every array a
+// kernel addresses through one stays below 2 GiB.
+constexpr int64_t kMaxResource = 0x7fffffff;
+
 int check_problem(const moe_w4a16_problem* p) {
   if (!p) return MOE_ERR_NULL;
   if (p->group_size != 32) return MOE_ERR_UNSUPPORTED;
@@ -32,6 +40,14 @@ int check_problem(const moe_w4a16_problem* p) {
   if (p->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->expert_base + p->num_experts > 0x7fffffff) return MOE_ERR_SHAPE;
   if (p->num_tokens > kMaxPairs / p->top_k) return MOE_ERR_SHAPE;
+  const int64_t H = p->hidden, I = p->inter;
+  // one bf16 matrix of the shared expert, one expert's int4 matrices
+  if (2 * I * H * 2 > kMaxResource) return MOE_ERR_UNSUPPORTED;
+  if (p->num_tokens > 0 && choose_block_m(p) != 4) {
+    // 96-row blocks: x (bf16 and fp16) and the bucketed h rows (fp16)
+    if (p->num_tokens * H * 2 > kMaxResource) return MOE_ERR_UNSUPPORTED;
+    if (sorted_capacity(p, choose_block_m(p)) * I * 2 > kMaxResource) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -43,15 +59,13 @@ int64_t sorted_capacity(const moe_w4a16_problem* p, int32_t bm) {
 
 int32_t choose_block_m(const moe_w4a16_problem* p) {
   // About one row per expert (decode): 4-row buckets and the weight-streaming
-  // small-batch kernels. Beyond that, the prefill kernel's blocks wherever its
-  // tiles fit the widths (measured faster than 16- and 64-row blocks from a
-  // few rows per expert on, and with skewed routing); else 64-row blocks with
-  // many rows per expert and 16-row blocks in between.
+  // small-batch kernels. Beyond that the block kernel's 96-row buckets
+  // (measured faster than 16- and 64-row blocks from a few rows per expert
+  // on, and with skewed routing).
   const int64_t P = p->num_tokens * p->top_k;
   const int64_t E = p->num_experts;
   if (P <= 4 * E && moe::small_batch_fits(p->hidden, p->inter)) return 4;
-  if (moe::prefill_fits(p->hidden, p->inter)) return moe::prefill_block_m();
-  return P >= 32 * E ? 64 : 16;
+  return moe::prefill_block_m();
 }
 
 // Bucketing in many work-groups (three launches) from this many pairs on.
@@ -61,9 +75,9 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
 constexpr int64_t kAlignMultiMin = MOE_ALIGN_MULTI_MIN;
 
 struct Layout {
-  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, shared_gu, blas, total;
+  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, x16, kx, kh, total;
   int64_t cap_rows;
-  int32_t max_blocks, bm;
+  int32_t max_blocks, bm, n_htiles;
 };
 
 Layout layout(const moe_w4a16_problem* p) {
@@ -71,6 +85,7 @@ Layout layout(const moe_w4a16_problem* p) {
   L.bm = choose_block_m(p);
   L.cap_rows = sorted_capacity(p, L.bm);
   L.max_blocks = (int32_t)(L.cap_rows / L.bm);
+  L.n_htiles = (p->inter + moe::kHTile - 1) / moe::kHTile;
   const size_t T = (size_t)p->num_tokens, H = (size_t)p->hidden, I = (size_t)p->inter;
   const size_t P = T * (size_t)p->top_k;
   size_t o = 0;
@@ -84,13 +99,13 @@ Layout layout(const moe_w4a16_problem* p) {
   L.align_scratch = o;
   if ((int64_t)P >= kAlignMultiMin)
     o = round_up(o + 4 * (size_t)moe::align_scratch_ints((int64_t)P, p->num_experts));
-  // prefill-sized blocks: the shared expert's gate/up output (fp32) and the
-  // library GEMM's workspace
-  L.shared_gu = L.blas = o;
+  // 96-row blocks: x in fp16 with its per-token exponents, the per-(row,
+  // tile) exponents of h
+  L.x16 = L.kx = L.kh = o;
   if (L.bm == moe::prefill_block_m()) {
-    o = round_up(o + 4 * T * 2 * I);
-    L.blas = o;
-    o = round_up(o + moe::kSharedBlasWorkspace);
+    L.x16 = o; o = round_up(o + 2 * T * H);
+    L.kx = o; o = round_up(o + 4 * T);
+    L.kh = o; o = round_up(o + 4 * (size_t)L.cap_rows * L.n_htiles);
   }
   L.total = o;
   return L;
@@ -227,39 +242,15 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
     err = moe::launch_align(topk_ids, T * k, E, p->expert_base, L.bm, sorted, blk, n_padded, strm);
   if (err != hipSuccess) return hip_status(err);
 
-  // One GEMM phase. Prefill blocks: the routed experts in the prefill kernel,
-  // the shared expert in a second launch of the tiled kernel (64-token tiles).
-  // Event `after_routed` is recorded once the routed experts' launch is
-  // queued (on the single-launch paths it follows the whole phase).
+  // One GEMM phase: a single launch that carries the routed experts and the
+  // shared expert. Event `after_routed` follows it.
   auto gemm = [&](const moe::GemmParams& gp, bool gate_up, int after_routed) -> hipError_t {
     hipError_t e;
-    if (L.bm == 4) {
+    if (L.bm == 4)
       e = gate_up ? moe::launch_gate_up_small(gp, strm) : moe::launch_down_small(gp, strm);
-      return e != hipSuccess ? e : mark(after_routed);
-    }
-    if (L.bm != moe::prefill_block_m()) {
-      e = gate_up ? moe::launch_gate_up(gp, L.bm, strm) : moe::launch_down(gp, L.bm, strm);
-      return e != hipSuccess ? e : mark(after_routed);
-    }
-    e = gate_up ? moe::launch_gate_up_prefill(gp, strm) : moe::launch_down_prefill(gp, strm);
-    if (e == hipSuccess) e = mark(after_routed);
-    if (e != hipSuccess || !gp.wshared) return e;
-    // the bf16 shared expert: dense GEMMs in hipBLASLt, SwiGLU in our kernel;
-    // where the library finds no algorithm, the tiled kernel below
-    if (gate_up) {
-      float* gu = reinterpret_cast<float*>(ws + L.shared_gu);
-      e = moe::launch_shared_blas(gp.wshared, gp.a_shared, gu, 2 * (int64_t)I, T, H, ws + L.blas,
-                                  strm);
-      if (e == hipSuccess) return moe::launch_swiglu(gu, gp.h_shared, T, I, strm);
-    } else {
-      e = moe::launch_shared_blas(gp.wshared, gp.a_shared, gp.y_shared, H, T, I, ws + L.blas,
-                                  strm);
-      if (e == hipSuccess) return e;
-    }
-    if (e != hipErrorNotSupported) return e;
-    moe::GemmParams gs = gp;
-    gs.max_blocks = 0;  // shared-expert tiles only
-    return gate_up ? moe::launch_gate_up(gs, 64, strm) : moe::launch_down(gs, 64, strm);
+    else
+      e = gate_up ? moe::launch_gate_up_prefill(gp, strm) : moe::launch_down_prefill(gp, strm);
+    return e != hipSuccess ? e : mark(after_routed);
   };
 
   moe::GemmParams g{};
@@ -273,9 +264,21 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.I = I;
   g.nibble_mask = 0x0F0F0F0Fu;
   g.prepacked = prepacked ? 1 : 0;
+  g.n_htiles = L.n_htiles;
+  const bool blocks96 = L.bm == moe::prefill_block_m();
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.x16);
+  int32_t* kx = reinterpret_cast<int32_t*>(ws + L.kx);
+  int32_t* kh = reinterpret_cast<int32_t*>(ws + L.kh);
 
-  // gate_up + SwiGLU
-  g.a_routed = static_cast<const uint16_t*>(x);
+  // gate_up + SwiGLU (96-row blocks: on x in fp16, converted first)
+  if ((err = mark(1)) != hipSuccess) return hip_status(err);
+  if (blocks96) {
+    err = moe::launch_x16(static_cast<const uint16_t*>(x), x16, kx, T, H, strm);
+    if (err != hipSuccess) return hip_status(err);
+  }
+  g.a_routed = blocks96 ? x16 : static_cast<const uint16_t*>(x);
+  g.a_exp = kx;
+  g.h_exp = kh;
   g.packed = packed_w13;
   g.scales = static_cast<const uint16_t*>(scales_w13);
   g.a_shared = static_cast<const uint16_t*>(x);
@@ -284,12 +287,13 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.h_shared = hs;
   g.K = H;
   g.N = I;
-  if ((err = mark(1)) != hipSuccess) return hip_status(err);
   err = gemm(g, true, 5);
   if (err != hipSuccess) return hip_status(err);
 
   // down
   g.a_routed = h;
+  g.a_exp = kh;
+  g.h_exp = nullptr;
   g.packed = packed_w2;
   g.scales = static_cast<const uint16_t*>(scales_w2);
   g.a_shared = hs;

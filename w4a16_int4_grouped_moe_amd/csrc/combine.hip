@@ -20,10 +20,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
@@ -96,21 +92,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   *reinterpret_cast<uint2*>(out + t * H + n) = o;
 }
 
-// SwiGLU of the shared expert's gate/up output (prefill-sized batches, where
-// its GEMMs run in the library): four columns per thread.
-__global__ __launch_bounds__(kThreads) void swiglu_kernel(const float* __restrict__ gu,
-                                                          uint16_t* __restrict__ h, int I) {
-  const int64_t t = blockIdx.x;
-  const int i = (blockIdx.y * kThreads + threadIdx.x) * 4;
-  if (i >= I) return;
-  const f32x4 g = *reinterpret_cast<const f32x4*>(gu + t * 2 * I + i);
-  const f32x4 u = *reinterpret_cast<const f32x4*>(gu + t * 2 * I + I + i);
-  uint2 o;
-  o.x = pack_bf16x2(silu_mul(g.x, u.x), silu_mul(g.y, u.y));
-  o.y = pack_bf16x2(silu_mul(g.z, u.z), silu_mul(g.w, u.w));
-  *reinterpret_cast<uint2*>(h + t * I + i) = o;
-}
-
 }  // namespace
 
 hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
@@ -125,14 +106,3 @@ hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_id
 
 }  // namespace moe
 
-namespace moe {
-
-hipError_t launch_swiglu(const float* gu, uint16_t* h, int64_t T, int32_t I, hipStream_t stream) {
-  if (T == 0) return hipSuccess;
-  if (I % 4 || T > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)T, (unsigned)((I / 4 + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL(swiglu_kernel, grid, dim3(kThreads), 0, stream, gu, h, I);
-  return hipGetLastError();
-}
-
-}  // namespace moe

@@ -1,26 +1,46 @@
 // gemm_prefill.hip -- grouped W4A16 GEMMs for many rows per expert (gfx950):
-// the int4 routed experts of prefill-sized batches, 96-row bucket blocks.
+// the int4 routed experts of every batch past the decode regime, in 96-row
+// bucket blocks, and the bf16 shared expert in 96-token tiles of the same
+// launches.
 //
-// Same two launches as the other GEMM paths (gate_up with the SwiGLU epilogue,
-// then down), for blocks of 96 bucketed rows of one expert. Here the layer is
-// a dense contraction per expert (about 85 rows each for 4096 tokens, top-8 of
+// Two launches per layer (after the bucketing and the activation conversion
+// below): gate_up with the SwiGLU epilogue, then down. Here the layer is a
+// dense contraction per expert (about 85 rows each for 4096 tokens, top-8 of
 // 384), so the kernel is built around keeping the MFMA pipes fed: every
-// dequantised weight serves all rows of the block, and all operands arrive
-// through LDS without holding registers while in flight.
+// dequantised weight serves all rows of the block, and the int4 operands
+// arrive through LDS without holding registers while in flight.
 //
-// Work-group (512 threads = 8 waves): one block of up to kBM bucketed rows x
-// 512 weight rows (a column tile; where K is only a few chunks, several
-// consecutive tiles of the block in turn, prefill_tiles_kernel). Every wave owns four 16-row weight sub-tiles (gate_up: two
-// gate sub-tiles and the two matching up sub-tiles) and computes them for all
-// of the block's rows, so each weight is dequantised exactly once per block.
-// K advances in chunks of 128 inputs (four 32-input groups). All operands reach
-// LDS through 16-byte buffer loads with an LDS destination (no registers held
-// while in flight), so registers hold only accumulators and the fragments of
-// one MFMA step:
+// Numerics: the int4 weights are exact. A code u of a group with scale s
+// (Kimi-K2.6 catalog entry, QUANT paragraph: symmetric, group 32) is the value
+// (u - 8) * s; with s a bf16 (8 significant bits) and |u - 8| <= 8 the product
+// has at most 11 significant bits, which is exactly an fp16 whenever
+// 2^-17 <= |s| <= 8188. So the routed products run on v_mfma_f32_16x16x32_f16:
+//  * activations x are converted once per call to fp16 with one power-of-two
+//    scale per token (x16_kernel: the largest |x| of the token lands in
+//    [2^14, 2^15)), which is exact for every value down to 2^-32 of the
+//    token's largest;
+//  * the SwiGLU output h is rounded once to fp16 with one power-of-two scale
+//    per (row, 256-column tile of gate_up), and the down launch rescales each
+//    tile to the row's largest scale while staging it (exact except values
+//    below 2^-38 of the row's largest);
+//  * the accumulators are fp32; the scales come back in the epilogues (exact
+//    power-of-two multiplies).
+// The bf16 shared expert keeps bf16 operands (bf16 MFMA, x as given, its h
+// rounded to bf16).
+//
+// Routed work-group (512 threads = 8 waves): one block of up to kBM bucketed
+// rows x 512 weight rows (a column tile; where K is only a few chunks, several
+// consecutive tiles of the block in turn, prefill_tiles_kernel). Every wave
+// owns four 16-row weight sub-tiles (gate_up: two gate sub-tiles and the two
+// matching up sub-tiles) and computes them for all of the block's rows, so
+// each weight is dequantised exactly once per block. K advances in chunks of
+// 128 inputs (four 32-input groups):
 //  * activations: the kBM x 128 chunk, double buffered; a row's 16 pieces of 16
 //    bytes are permuted, piece c of row r at slot c ^ f(r & 15) where f swaps
 //    the two 2-bit halves of its argument, so that the fragment reads (16 rows
-//    at one k offset per 16 lanes) are free of bank conflicts;
+//    at one k offset per 16 lanes) are free of bank conflicts. gate_up copies
+//    them straight from HBM into LDS (buffer loads with an LDS destination);
+//    down loads its h rows into registers, rescales them and writes them;
 //  * weights: the 512 rows x 64 bytes (four groups of 32 codes) of the chunk,
 //    double buffered, the four groups of row r permuted by (r >> 1) & 3 for the
 //    same reason; lane (r = lane % 16, q = lane / 16) of a wave reads group q of
@@ -29,17 +49,23 @@
 //    reads, where the simpler XOR forms are not)
 //  * scales: 16 groups (4 chunks) of each of the 512 rows, two buffers that
 //    alternate every 4 chunks;
-//  * the words are dequantised to bf16 (u - 8) * s and fed to
-//    v_mfma_f32_16x16x32_bf16: MFMA step j of a chunk takes word j of every
-//    lane, so its 32-long reduction covers one 8-input slice of each of the
-//    four groups; the matching activations are read at those offsets. The
-//    next step's dequantisation (VALU) is interleaved with this step's MFMAs.
+//  * the words are dequantised to fp16 (u - 8) * s and fed to the MFMA: step j
+//    of a chunk takes word j of every lane, so its 32-long reduction covers one
+//    8-input slice of each of the four groups; the matching activations are
+//    read at those offsets. The next step's dequantisation (VALU) is
+//    interleaved with this step's MFMAs.
 // One barrier per chunk: the copies of chunk c + 1 are issued during the first
-// MFMA step of chunk c and waited for after it. Barriers are raw s_barrier with explicit
-// waits (the fence of __syncthreads() would also wait for the copies just
-// issued). The number of 16-row sub-tiles holding bucket rows (even, after
-// rounding up) is a template parameter of the K loop, so the loop body is
-// straight-line code.
+// MFMA step of chunk c and waited for after it. Barriers are raw s_barrier with
+// explicit waits (the fence of __syncthreads() would also wait for the copies
+// just issued). The number of 16-row sub-tiles holding bucket rows (even,
+// after rounding up) is a template parameter of the K loop, so the loop body
+// is straight-line code. Widths that are not whole tiles (hidden % 512,
+// inter % 256) run masked: weight rows past the width read zeros and their
+// outputs are not stored.
+//
+// Shared-expert work-group: 96 tokens x 512 weight rows, activations through
+// LDS as above (bf16, rows = tokens), each wave streams its own bf16 weight
+// rows into registers, three MFMA steps ahead.
 #include "internal.h"
 
 namespace moe {
@@ -55,12 +81,13 @@ namespace {
 constexpr int kPrefillAux = MOE_PREFILL_AUX;
 constexpr int kPrefillPackedAux = 2;
 
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 #ifndef MOE_PREFILL_MAX_SUBTILES
@@ -82,7 +109,9 @@ constexpr int kSRowBytes = kSPeriod * 4 * 2;  // scale bytes of one row per buff
 constexpr int kSBytes = kBN * kSRowBytes;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 static_assert(kBN == kPackRows && kKC == kPackChunk, "tiles of the prepacked layout");
+static_assert(kHTile == kBN / 2, "h exponent tiles are the gate_up column tiles");
 constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
+constexpr int kSharedAhead = 3;            // MFMA steps of shared weights in flight
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -92,6 +121,12 @@ __shared__ __attribute__((aligned(1024))) uint8_t lds_w0[kWBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kWBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kSBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_s1[kSBytes];
+// per block row: the exponent of its activation scale (gate_up: the token's;
+// down: the row's largest h tile exponent), the h tile exponent being chosen,
+// and the per-wave maxima it is chosen from
+__shared__ int32_t lds_rexp[kBM];
+__shared__ int32_t lds_rkh[kBM];
+__shared__ float lds_rmax[kWaves][kBM];
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -109,52 +144,71 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
 }
 
-// Per-group dequantisation constants: the scale s, -1032 s, s / 16 and -72 s.
-struct GroupScale {
-  float s, c1032, s16, c72;
-};
-__device__ __forceinline__ GroupScale group_scale(float s) {
-  return GroupScale{s, -1032.0f * s, 0.0625f * s, -72.0f * s};
+// A bf16 group scale as an fp16 pair (exact for 2^-17 <= |s| <= 65504).
+__device__ __forceinline__ h16x2 scale_pair(uint32_t bits) {
+  const _Float16 h = (_Float16)bf16_to_f32(bits);
+  return h16x2{h, h};
 }
 
-// The eight codes of one word -> eight bf16 weights (u - 8) * s in input order.
+// The eight codes of one word -> eight fp16 weights (u - 8) * s, in the order
+// of fields 0, 4, 1, 5, 2, 6, 3, 7 (activations are stored in the same order).
 // A field in bits 0-3 of a 16-bit half OR-ed into the fp16 pattern 0x6400 is
-// exactly the fp16 value 1024 + u, a field in bits 4-7 gives 1024 + 16 u, so
-// the word's low byte pair (fields 0, 4 and 1, 5) needs no shift and its high
-// byte pair (fields 2, 6 and 3, 7) one shift by 8: one shift and four
-// v_bitop3 per word. One mixed fp16/fp32 FMA per code, fma(1024 + u, s,
-// -1032 s) or fma(1024 + 16 u, s / 16, -72 s), gives (u - 8) * s exactly in
-// fp32 (the products have at most 19 significant bits, and s / 16, 1032 s and
-// 72 s are exact), which is rounded once to bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, const GroupScale& g) {
+// exactly 1024 + u, a field in bits 4-7 gives 1024 + 16 u: the word's low
+// byte pair (fields 0, 4 and 1, 5) needs no shift, its high byte pair (fields
+// 2, 6 and 3, 7) one shift by 8. (1024 + u) - 1032 and (1024 + 16 u) / 16 - 72
+// are exactly u - 8, and (u - 8) * s is exact in fp16 (at most 11 significant
+// bits). 13 VALU instructions per word (one shift, four v_bitop3, four packed
+// fp16 add/fma, four packed fp16 multiplies).
+__device__ __forceinline__ h16x8 dequant8(uint32_t w, h16x2 s2) {
   const uint32_t w8 = w >> 8;
+  const h16x2 c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h16x2 c16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h16x2 c72 = {(_Float16)-72.0f, (_Float16)-72.0f};
   const h16x2 h0 = __builtin_bit_cast(h16x2, and_or(w, 0x000F000Fu, 0x64006400u));   // u0, u4
   const h16x2 h1 = __builtin_bit_cast(h16x2, and_or(w, 0x00F000F0u, 0x64006400u));   // u1, u5
   const h16x2 h2 = __builtin_bit_cast(h16x2, and_or(w8, 0x000F000Fu, 0x64006400u));  // u2, u6
   const h16x2 h3 = __builtin_bit_cast(h16x2, and_or(w8, 0x00F000F0u, 0x64006400u));  // u3, u7
-  const f32x2 v0 = {fmaf((float)h0[0], g.s, g.c1032), fmaf((float)h0[1], g.s, g.c1032)};
-  const f32x2 v1 = {fmaf((float)h1[0], g.s16, g.c72), fmaf((float)h1[1], g.s16, g.c72)};
-  const f32x2 v2 = {fmaf((float)h2[0], g.s, g.c1032), fmaf((float)h2[1], g.s, g.c1032)};
-  const f32x2 v3 = {fmaf((float)h3[0], g.s16, g.c72), fmaf((float)h3[1], g.s16, g.c72)};
-  u32x4 r;
-  r[0] = pack_bf16x2(v0[0], v1[0]);
-  r[1] = pack_bf16x2(v2[0], v3[0]);
-  r[2] = pack_bf16x2(v0[1], v1[1]);
-  r[3] = pack_bf16x2(v2[1], v3[1]);
-  return __builtin_bit_cast(bf16x8, r);
+  const h16x2 q0 = (h0 + c1032) * s2;
+  const h16x2 q1 = __builtin_elementwise_fma(h1, c16, c72) * s2;
+  const h16x2 q2 = (h2 + c1032) * s2;
+  const h16x2 q3 = __builtin_elementwise_fma(h3, c16, c72) * s2;
+  return h16x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
+// Position of input c inside its stored 8-element piece: fields 0..7 are
+// stored in the order 0, 4, 1, 5, 2, 6, 3, 7.
+__device__ __forceinline__ int perm_pos(int c) {
+  const int j = c & 7;
+  return (c & ~7) | ((j & 3) << 1) | (j >> 2);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Exponent k with m * 2^-k in [2^14, 2^15) for a positive finite m; 0
+// otherwise (zero rows; rows holding inf or NaN keep them).
+__device__ __forceinline__ int scale_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.0e38f)) return 0;
+  return __builtin_amdgcn_frexp_expf(m) - 15;
+}
+
+// largest value over the 16 lanes of a row of the wave (lanes 16q..16q+15)
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 16));
+  v = fmaxf(v, __shfl_xor(v, 2, 16));
+  v = fmaxf(v, __shfl_xor(v, 4, 16));
+  v = fmaxf(v, __shfl_xor(v, 8, 16));
+  return v;
+}
+
 // s_waitcnt with only the vector-memory counter limited (lgkm and exp left
-// unconstrained), and with both vector-memory and LDS counters at zero.
+// unconstrained), and with the LDS counter at zero.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -166,17 +220,70 @@ constexpr int tile_cols() { return PHASE == kGateUp ? kBN / 2 : kBN; }
 __device__ __forceinline__ int wslot(int R) { return (R >> 1) & 3; }
 __device__ __forceinline__ int aslot(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Weight row of work-group row R = 64 wave + 16 sub-tile + r.
+// Output column (h column for gate_up, y column for down) of work-group row
+// R = 64 wave + 16 sub-tile + r; gate_up sub-tiles 0, 1 are gate rows, 2, 3
+// the matching up rows.
 template <int PHASE>
-__device__ __forceinline__ int weight_row(const GemmParams& p, int tile, int R) {
+__device__ __forceinline__ int out_col(int tile, int R) {
   const int w = R >> 6, s = (R >> 4) & 3, r = R & 15;
-  if (PHASE == kGateUp) {
-    const int c = tile * (kBN / 2) + w * 32 + 16 * (s & 1) + r;
-    return s < 2 ? c : p.I + c;  // gate rows, then the matching up rows
-  }
+  if (PHASE == kGateUp) return tile * (kBN / 2) + w * 32 + 16 * (s & 1) + r;
   return tile * kBN + w * 64 + 16 * s + r;
 }
+// Weight row of work-group row R, or -1 past the width.
+template <int PHASE>
+__device__ __forceinline__ int weight_row(const GemmParams& p, int tile, int R) {
+  const int c = out_col<PHASE>(tile, R);
+  if (PHASE == kGateUp) {
+    if (c >= p.I) return -1;
+    return ((R >> 4) & 3) < 2 ? c : p.I + c;  // gate rows, then the matching up rows
+  }
+  return c < p.N ? c : -1;
+}
 
+// ---- the x conversion --------------------------------------------------------
+// x16[t] = fp16(x[t] * 2^-kx[t]) in the stored piece order, kx[t] chosen from
+// the token's largest finite |x| (one work-group per token).
+constexpr int kConvThreads = 256;
+
+__global__ __launch_bounds__(kConvThreads) void x16_kernel(const uint16_t* __restrict__ x,
+                                                           uint16_t* __restrict__ x16,
+                                                           int32_t* __restrict__ kx, int H) {
+  __shared__ uint32_t wmax[kConvThreads / 64];
+  const int64_t t = blockIdx.x;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + t * H);
+  u32x4* dst = reinterpret_cast<u32x4*>(x16 + t * H);
+  const int npieces = H / 8;
+  uint32_t m = 0;
+  for (int g = threadIdx.x; g < npieces; g += kConvThreads) {
+    const u32x4 v = src[g];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = v[d] & 0x7FFFu, hi = (v[d] >> 16) & 0x7FFFu;
+      if (lo < 0x7F80u) m = max(m, lo);  // finite values only
+      if (hi < 0x7F80u) m = max(m, hi);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int k = scale_exp(bf16_to_f32(m));
+  if (threadIdx.x == 0) kx[t] = k;
+  for (int g = threadIdx.x; g < npieces; g += kConvThreads) {
+    const u32x4 v = src[g];
+    _Float16 h[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      h[2 * d] = (_Float16)__builtin_ldexpf(bf16_to_f32(v[d] & 0xFFFFu), -k);
+      h[2 * d + 1] = (_Float16)__builtin_ldexpf(bf16_to_f32(v[d] >> 16), -k);
+    }
+    // stored order: inputs 0, 4, 1, 5, 2, 6, 3, 7 of the piece
+    const h16x8 o = {h[0], h[4], h[1], h[5], h[2], h[6], h[3], h[7]};
+    dst[g] = __builtin_bit_cast(u32x4, o);
+  }
+}
+
+// ---- routed int4 blocks ---------------------------------------------------------
 // MT: the work-group computes ntl consecutive column tiles of the block
 // (otherwise exactly one: ntl is then the constant 1)
 template <int PHASE, int MS, bool PK, bool MT>
@@ -194,45 +301,101 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
   const int64_t wbase = (int64_t)e * Nw;
 
-  // ---- activation copies: instruction t covers LDS rows 4t..4t+3 ------------
+  // ---- activation chunk c of tile t ------------------------------------------
+  // gate_up: x16 rows gathered by pair, copied into LDS by buffer loads with an
+  // LDS destination; instruction t covers LDS rows 4t..4t+3.
   constexpr int kACopies = kBM / 4;                        // per work-group
   constexpr int kAPerWave = (kACopies + kWaves - 1) / kWaves;
+  // down: thread t loads piece t % 16 of rows t / 16 + 32 i into registers,
+  // rescales them to the row's largest h tile exponent and writes them.
+  constexpr int kARows = kBM * 16 / kThreads;
+  static_assert(kBM * 16 % kThreads == 0, "down staging rows per thread");
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a_routed, 0,
       (int)((PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM) * K * 2), kBufferFlags);
-  uint32_t aoff[kAPerWave];
-#pragma unroll
-  for (int i = 0; i < kAPerWave; ++i) {
-    const int t = kAPerWave * wave + i;
-    const int row = 4 * t + (lane >> 4);
-    const int piece = (lane & 15) ^ aslot(row & 15);
-    int64_t src = -1;
-    if (t < kACopies && row < MS * 16) {
-      if (PHASE == kGateUp) {
-        const int32_t pair = p.sorted_ids[row0 + row];
-        if (pair < p.P) src = pair / p.k;
-      } else {
-        src = row0 + row;
-      }
-    }
-    aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
-  }
-  // copies are addressed by (tile t of the work-group's tiles, chunk c of it);
-  // past the last tile an offset beyond any buffer (loads zeros)
-  auto copy_a = [&](uint8_t* dst, int t, int c) {
-    const int so = uniform(t < ntl ? c * kKC * 2 : (int)kNoRow);
+  uint32_t aoff[PHASE == kGateUp ? kAPerWave : kARows];
+  int kref[kARows];
+  const int apiece = tid & 15, arow = tid >> 4;
+  if (PHASE == kGateUp) {
 #pragma unroll
     for (int i = 0; i < kAPerWave; ++i) {
       const int t = kAPerWave * wave + i;
-      if (kACopies % kWaves == 0 || t < kACopies)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + t * 1024), 16, aoff[i], so, 0, 0);
+      const int row = 4 * t + (lane >> 4);
+      const int piece = (lane & 15) ^ aslot(row & 15);
+      int64_t src = -1;
+      if (t < kACopies && row < MS * 16) {
+        const int32_t pair = p.sorted_ids[row0 + row];
+        if (pair < p.P) src = pair / p.k;
+      }
+      aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kARows; ++i) {
+      const int r = arow + 32 * i;
+      aoff[i] = r < MS * 16 ? (uint32_t)(((row0 + r) * K + apiece * 8) * 2) : kNoRow;
+      int m = -1000;
+      if (r < MS * 16) {
+        const int32_t* ke = p.a_exp + (row0 + r) * p.n_htiles;
+        for (int j = 0; j < p.n_htiles; ++j) m = max(m, ke[j]);
+      }
+      kref[i] = m;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_exp, 0,
+      PHASE == kGateUp ? 0 : (int)((int64_t)p.max_blocks * kBM * p.n_htiles * 4), kBufferFlags);
+  u32x4 areg[kARows];
+  int kreg[kARows];
+  auto copy_a = [&](uint8_t* dst, int t, int c) {
+    if (PHASE == kGateUp) {
+      const int so = uniform(t < ntl ? c * kKC * 2 : (int)kNoRow);
+#pragma unroll
+      for (int i = 0; i < kAPerWave; ++i) {
+        const int tt = kAPerWave * wave + i;
+        if (kACopies % kWaves == 0 || tt < kACopies)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + tt * 1024), 16, aoff[i],
+                                                   so, 0, 0);
+      }
+    } else {
+      // loads into registers; the h tile exponents of the chunk's rows with them
+      const int so = uniform(t < ntl ? c * kKC * 2 : (int)kNoRow);
+      const int ko = uniform(t < ntl ? (c * kKC / kHTile) * 4 : (int)kNoRow);
+#pragma unroll
+      for (int i = 0; i < kARows; ++i) {
+        areg[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[i], so, 0));
+        const int r = arow + 32 * i;
+        kreg[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+            kres, r < MS * 16 ? (uint32_t)((row0 + r) * p.n_htiles * 4) : kNoRow, ko, 0);
+      }
+    }
+  };
+  // down: the loaded pieces, rescaled by 2^(tile exponent - row exponent) <= 1,
+  // into LDS (after the loads have been waited for)
+  auto store_a = [&](uint8_t* dst) {
+    if (PHASE == kDown) {
+#pragma unroll
+      for (int i = 0; i < kARows; ++i) {
+        const int r = arow + 32 * i;
+        if (r < MS * 16) {
+          // (the whole 16-byte piece is reinterpreted at once: a bit_cast of
+          // a single element of an ext_vector value miscompiles with this
+          // compiler, reading element 0 for every element)
+          const _Float16 f = (_Float16)__builtin_ldexpf(1.0f, kreg[i] - kref[i]);
+          const h16x8 f8 = {f, f, f, f, f, f, f, f};
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_bit_cast(h16x8, areg[i]) * f8);
+          *reinterpret_cast<u32x4*>(dst + r * (kKC * 2) + ((apiece ^ aslot(r & 15)) * 16)) = v;
+        }
+      }
     }
   };
 
   // ---- weight copies: instruction u covers rows 16u..16u+15 (64 B each) ------
   // Checkpoint layout: row R's 64 bytes of chunk ch at ch * 64 in its row of
   // K / 2 bytes. Prepacked layout: the tile's chunk is one 32 KB run (rows of
-  // 64 bytes), so an instruction reads 1 KB of whole lines.
+  // 64 bytes), so an instruction reads 1 KB of whole lines. Rows past the
+  // width read zeros.
   constexpr bool packed_layout = PK;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + wbase * (K / 8)), 0, Nw * (K / 8) * 4, kBufferFlags);
@@ -241,12 +404,13 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   for (int i = 0; i < 4; ++i) {
     const int R = 16 * (4 * wave + i) + (lane >> 2);
     const int g = (lane & 3) ^ wslot(R);
-    woff[i] = packed_layout
-                  ? (uint32_t)(((tile * nch) * kBN + R) * kWRowBytes + 16 * g)
-                  : (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 8) + 4 * g) * 4);
+    const int n = weight_row<PHASE>(p, tile, R);
+    woff[i] = n < 0 ? kNoRow
+              : packed_layout ? (uint32_t)(((tile * nch) * kBN + R) * kWRowBytes + 16 * g)
+                              : (uint32_t)((n * (K / 8) + 4 * g) * 4);
   }
   const int wstep = packed_layout ? kWBytes : kWRowBytes;  // bytes per chunk
-  // bytes from one tile's weights to the next tile's
+  // bytes from one tile's weights to the next tile's (whole tiles only)
   const int wtile = packed_layout ? nch * kWBytes : tile_cols<PHASE>() * (K / 2);
   auto copy_w = [&](uint8_t* dst, int t, int c) {
     const int so = uniform(t < ntl ? t * wtile + c * wstep : (int)kNoRow);
@@ -272,9 +436,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int R = 32 * (2 * wave + i) + (lane >> 1);
-    soff[i] = packed_layout
-                  ? (uint32_t)(((tile * nper) * kBN + R) * kSRowBytes + 16 * (lane & 1))
-                  : (uint32_t)((weight_row<PHASE>(p, tile, R) * (K / 32) + 8 * (lane & 1)) * 2);
+    const int n = weight_row<PHASE>(p, tile, R);
+    soff[i] = n < 0 ? kNoRow
+              : packed_layout ? (uint32_t)(((tile * nper) * kBN + R) * kSRowBytes + 16 * (lane & 1))
+                              : (uint32_t)((n * (K / 32) + 8 * (lane & 1)) * 2);
   }
   const int sstep = packed_layout ? kSBytes : kSRowBytes;  // bytes per period
   const int stile = packed_layout ? nper * kSBytes : tile_cols<PHASE>() * (K / 16);
@@ -296,9 +461,25 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   }
   // scales: row R, group 4 (chunk % 4) + lq
   const int sread = (wave * 64 + lr) * kSRowBytes + lq * 2;
-  constexpr int kMaxCopies = kAPerWave + 4 + 2;  // copy instructions per wave and chunk
+  constexpr int kACopyInstr = PHASE == kGateUp ? kAPerWave : 2 * kARows;
+  constexpr int kMaxCopies = kACopyInstr + 4 + 2;  // copy instructions per wave and chunk
   // activations: row 16 mi + lr, piece 4 lq + j (permuted slot)
   const int aread = lr * (kKC * 2);
+
+  // per-row activation exponents (gate_up: the token's; down: the row's
+  // largest h tile exponent), before the first barrier
+  if (tid < kBM) {
+    int v = 0;
+    if (PHASE == kGateUp) {
+      const int32_t pair = p.sorted_ids[row0 + tid];
+      if (pair < p.P) v = p.a_exp[pair / p.k];
+    } else if (tid < MS * 16) {
+      const int32_t* ke = p.a_exp + (row0 + tid) * p.n_htiles;
+      v = ke[0];
+      for (int j = 1; j < p.n_htiles; ++j) v = max(v, ke[j]);
+    }
+    lds_rexp[tid] = v;
+  }
 
   f32x4 acc[MS][kNSub];
 #pragma unroll
@@ -308,31 +489,28 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 
   // issue_copies() is called in the first MFMA step; the scheduler spreads its
   // copy instructions between that step's MFMAs.
-  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const float (&sc)[kNSub],
+  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const h16x2 (&sc)[kNSub],
                      auto&& issue_copies) {
-    GroupScale gs[kNSub];
+    h16x8 bw[2][kNSub];  // this step's and the next step's weights
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) gs[s] = group_scale(sc[s]);
-    bf16x8 bw[2][kNSub];  // this step's and the next step's weights
-#pragma unroll
-    for (int s = 0; s < kNSub; ++s) bw[0][s] = dequant8(w[s][0], gs[s]);
+    for (int s = 0; s < kNSub; ++s) bw[0][s] = dequant8(w[s][0], sc[s]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      bf16x8 a[MS];
-      const int apiece = ((4 * lq + j) ^ aslot(lr)) * 16;  // inputs 32 lq + 8 j
+      h16x8 a[MS];
+      const int apc = ((4 * lq + j) ^ aslot(lr)) * 16;  // inputs 32 lq + 8 j
 #pragma unroll
       for (int mi = 0; mi < MS; ++mi)
-        a[mi] = *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apiece);
+        a[mi] = *reinterpret_cast<const h16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apc);
       if (j < 3) {
 #pragma unroll
         for (int s = 0; s < kNSub; ++s)
-          bw[(j + 1) & 1][s] = dequant8(w[s][j + 1], gs[s]);
+          bw[(j + 1) & 1][s] = dequant8(w[s][j + 1], sc[s]);
       }
 #pragma unroll
       for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
         for (int s = 0; s < kNSub; ++s)
-          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], bw[j & 1][s], acc[mi][s], 0, 0, 0);
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], bw[j & 1][s], acc[mi][s], 0, 0, 0);
       if (j == 0) issue_copies();
       // interleave: the activation reads first, then one MFMA per three VALU
       // instructions of the next step's dequantisation, and in the first step
@@ -347,13 +525,13 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_scales = [&](float (&sc)[kNSub], int t, int c) {
+  auto read_scales = [&](h16x2 (&sc)[kNSub], int t, int c) {
     const int per = t * nper + c / kSPeriod;  // period count across the tiles
     const uint8_t* sb = (per & 1) ? lds_s1 : lds_s0;
     const int g = (c % kSPeriod) * 8;  // bytes: 4 groups per chunk
 #pragma unroll
     for (int s = 0; s < kNSub; ++s)
-      sc[s] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sb + sread + s * 16 * kSRowBytes + g));
+      sc[s] = scale_pair(*reinterpret_cast<const uint16_t*>(sb + sread + s * 16 * kSRowBytes + g));
   };
 
   // The chunk's scales and this wave's weight words are read from LDS first;
@@ -364,15 +542,16 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // step's MFMAs, not as one burst after the barrier: a burst from all eight
   // waves at once stalls them on issue with no MFMA work in flight.
   auto chunk = [&](int t, int c, uint8_t* abuf, uint8_t* anext, uint8_t* wbuf) {
-    float sc[kNSub];
+    h16x2 sc[kNSub];
     read_scales(sc, t, c);
     u32x4 w[kNSub];
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread[s]);
     wait_lgkm0();
     __builtin_amdgcn_sched_barrier(0);
-    // the chunk after this one and the one after that (nch is even, so a
-    // tile boundary falls between two chunks of a pair)
+    // the chunk after this one and the one after that (multi-tile work-groups
+    // have an even chunk count, so a tile boundary falls between two chunks of
+    // a pair)
     const int t1 = c + 1 < nch ? t : t + 1, c1 = c + 1 < nch ? c + 1 : 0;
     const int t2 = c + 2 < nch ? t : t + 1, c2 = c + 2 < nch ? c + 2 : c + 2 - nch;
     // the next scale period, at the first chunk of each period
@@ -385,35 +564,75 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       copy_w(wbuf, t2, c2);
       if (new_s) copy_s(pbuf ? lds_s1 : lds_s0, tn, lpn);
     });
-    // activations and weights of chunk ch + 1 in LDS (the copies of chunk
-    // ch + 2's weights and of the next scales may stay in flight); this
-    // chunk's LDS reads done before its activation buffer is overwritten
+    // activations and weights of chunk ch + 1 in LDS or registers (the copies
+    // of chunk ch + 2's weights and of the next scales may stay in flight);
+    // this chunk's LDS reads done before its activation buffer is overwritten
     if (new_s) wait_vm<6>();
     else wait_vm<4>();
+    store_a(anext);
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
   };
 
   // ---- pipeline -----------------------------------------------------------
+  copy_a(lds_a0, 0, 0);
   copy_w(lds_w0, 0, 0);
   copy_w(lds_w1, 0, 1);
-  copy_a(lds_a0, 0, 0);
   copy_s(lds_s0, 0, 0);
   wait_vm<0>();
+  store_a(lds_a0);
+  wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   // ---- epilogue: lane holds rows 4 lq + i of each 16-row sub-tile, column lr
   auto epilogue = [&](int ctile) {
     if (PHASE == kGateUp) {
+      // h = silu(g) * u at the true scale (activations came scaled by 2^-kx),
+      // then one power-of-two scale per row of the tile, from the row's
+      // largest |h| over the tile's 256 columns
+      float rmax[MS][4];
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kx = lds_rexp[mi * 16 + 4 * lq + i];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const float g = __builtin_ldexpf(acc[mi][s][i], kx);
+            const float u = __builtin_ldexpf(acc[mi][s + 2][i], kx);
+            acc[mi][s][i] = silu_mul(g, u);
+          }
+          rmax[mi][i] = max16(fmaxf(fabsf(acc[mi][0][i]), fabsf(acc[mi][1][i])));
+        }
+      if (lr == 0) {
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lds_rmax[wave][mi * 16 + 4 * lq + i] = rmax[mi][i];
+      }
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      if (tid < MS * 16) {
+        float m = lds_rmax[0][tid];
+#pragma unroll
+        for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, lds_rmax[w2][tid]);
+        const int kh = scale_exp(m);
+        lds_rkh[tid] = kh;
+        p.h_exp[(row0 + tid) * p.n_htiles + ctile] = kh;
+      }
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      _Float16* h16 = reinterpret_cast<_Float16*>(p.h_routed);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int col = ctile * (kBN / 2) + wave * 32 + 16 * s + lr;
+        if (col >= p.I) continue;
+        const int pc = perm_pos(col);
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int64_t r = row0 + mi * 16 + 4 * lq + i;
-            const float hv = silu_mul(acc[mi][s][i], acc[mi][s + 2][i]);
-            p.h_routed[r * p.I + col] = (uint16_t)(pack_bf16x2(hv, 0.f) & 0xFFFFu);
+            const int r = mi * 16 + 4 * lq + i;
+            h16[(row0 + r) * p.I + pc] = (_Float16)__builtin_ldexpf(acc[mi][s][i], -lds_rkh[r]);
           }
       }
     } else {
@@ -421,39 +640,189 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t r = row0 + mi * 16 + 4 * lq + i;
-          const int32_t pair = p.sorted_ids[r];
+          const int r = mi * 16 + 4 * lq + i;
+          const int64_t row = row0 + r;
+          const int32_t pair = p.sorted_ids[row];
           if (pair >= p.P) continue;
-          float* dst = p.y_routed + (int64_t)pair * p.N + ctile * kBN + wave * 64 + lr;
+          const int kr = lds_rexp[r];
+          float* dst = p.y_routed + (int64_t)pair * p.N;
 #pragma unroll
-          for (int s = 0; s < kNSub; ++s) dst[16 * s] = acc[mi][s][i];
+          for (int s = 0; s < kNSub; ++s) {
+            const int col = ctile * kBN + wave * 64 + 16 * s + lr;
+            if (col < p.N) dst[col] = __builtin_ldexpf(acc[mi][s][i], kr);
+          }
         }
     }
   };
 
-  // whole pairs (the chunk count is even; a loop with a second exit between
-  // the halves makes the register allocator move the accumulators)
+  // one chunk per iteration, the buffers chosen by the chunk's parity (a
+  // body of two chunks plus an odd last one, three inlined copies, made the
+  // register allocator spill)
   if (!MT) {
-    for (int c = 0; c < nch; c += 2) {
-      chunk(0, c, lds_a0, lds_a1, lds_w0);
-      chunk(0, c + 1, lds_a1, lds_a0, lds_w1);
+    for (int c = 0; c < nch; ++c) {
+      const bool odd = c & 1;
+      chunk(0, c, odd ? lds_a1 : lds_a0, odd ? lds_a0 : lds_a1, odd ? lds_w1 : lds_w0);
     }
     epilogue(tile);
     return;
   }
   // several tiles: they follow each other without a break in the copy
   // stream (the last chunks of a tile already fetch the next tile's first
-  // ones); the accumulators restart at zero for each tile
+  // ones); the accumulators restart at zero for each tile. The chunk count is
+  // even, so the parity of c is that of the chunk count so far.
   for (int t = 0; t < ntl; ++t) {
-    for (int c = 0; c < nch; c += 2) {
-      chunk(t, c, lds_a0, lds_a1, lds_w0);
-      chunk(t, c + 1, lds_a1, lds_a0, lds_w1);
+    for (int c = 0; c < nch; ++c) {
+      const bool odd = c & 1;
+      chunk(t, c, odd ? lds_a1 : lds_a0, odd ? lds_a0 : lds_a1, odd ? lds_w1 : lds_w0);
     }
     epilogue(tile + t);
 #pragma unroll
     for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
       for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// ---- shared-expert tiles (bf16 weights) -----------------------------------------
+// A work-group: 96 tokens (t0..) x 512 weight rows of the shared expert's
+// gate/up [2I, H] (gate_up; sub-tiles as in the routed blocks) or down [H, I].
+// Activations (x or the shared h, bf16) through LDS as in the routed blocks;
+// every lane loads, per MFMA step and sub-tile, the 16 bytes of its weight row
+// at inputs 32 lq + 8 j of the chunk (the fragment the routed layout reads at
+// that step), kSharedAhead steps ahead of their use.
+template <int PHASE, int MS>
+__device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int tile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int K = p.K;
+  const int nch = K / kKC;
+  const int nsteps = 4 * nch;
+  const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
+
+  constexpr int kACopies = kBM / 4;
+  constexpr int kAPerWave = (kACopies + kWaves - 1) / kWaves;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_shared, 0, (int)(p.T * K * 2), kBufferFlags);
+  uint32_t aoff[kAPerWave];
+#pragma unroll
+  for (int i = 0; i < kAPerWave; ++i) {
+    const int t = kAPerWave * wave + i;
+    const int row = 4 * t + (lane >> 4);
+    const int piece = (lane & 15) ^ aslot(row & 15);
+    const int64_t tok = t0 + row;
+    aoff[i] = (t < kACopies && row < MS * 16 && tok < p.T) ? (uint32_t)((tok * K + piece * 8) * 2)
+                                                            : kNoRow;
+  }
+  auto copy_a = [&](uint8_t* dst, int c) {
+    const int so = uniform(c < nch ? c * kKC * 2 : (int)kNoRow);
+#pragma unroll
+    for (int i = 0; i < kAPerWave; ++i) {
+      const int tt = kAPerWave * wave + i;
+      if (kACopies % kWaves == 0 || tt < kACopies)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + tt * 1024), 16, aoff[i], so,
+                                                 0, 0);
+    }
+  };
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
+  uint32_t woff[kNSub];
+#pragma unroll
+  for (int s = 0; s < kNSub; ++s) {
+    const int n = weight_row<PHASE>(p, tile, wave * 64 + 16 * s + lr);
+    woff[s] = n < 0 ? kNoRow : (uint32_t)((n * K + 32 * lq) * 2);
+  }
+  // weights of step q = 4 c + j: inputs 128 c + 32 lq + 8 j .. + 8
+  bf16x8 wring[kSharedAhead + 1][kNSub];
+  auto load_w = [&](bf16x8 (&dst)[kNSub], int q) {
+    const int so = uniform(q < nsteps ? ((q >> 2) * kKC + 8 * (q & 3)) * 2 : (int)kNoRow);
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s)
+      dst[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], so, 0));
+  };
+  const int aread = lr * (kKC * 2);
+
+  f32x4 acc[MS][kNSub];
+#pragma unroll
+  for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  copy_a(lds_a0, 0);
+#pragma unroll
+  for (int q = 0; q < kSharedAhead; ++q) load_w(wring[q], q);
+  wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+
+  // One chunk: four steps; the activation copy of chunk c + 1 is issued before
+  // the weight loads of the first step, the weight loads of step q +
+  // kSharedAhead at each step q. Loads complete in issue order, so the wait
+  // before step j leaves in flight the weight loads issued after step q's
+  // (and, for the first steps, the activation copy issued among them).
+  auto chunk = [&](int c, const uint8_t* abuf, uint8_t* anext) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * c + j;
+      if (j == 0) copy_a(anext, c + 1);
+      load_w(wring[(j + kSharedAhead) & 3], q + kSharedAhead);
+      if (j < kSharedAhead) wait_vm<4 * kSharedAhead + kAPerWave>();
+      else wait_vm<4 * kSharedAhead>();
+      bf16x8 a[MS];
+      const int apc = ((4 * lq + j) ^ aslot(lr)) * 16;
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+        a[mi] = *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apc);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s)
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], wring[j & 3][s], acc[mi][s],
+                                                               0, 0, 0);
+    }
+    // the activation copy of chunk c + 1 done (the weight loads of the next
+    // kSharedAhead steps may stay in flight); this chunk's LDS reads done
+    wait_vm<4 * kSharedAhead>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+  static_assert(kSharedAhead + 1 == 4, "the weight ring has one slot per step of a chunk");
+  for (int c = 0; c < nch; ++c) {
+    const bool odd = c & 1;
+    chunk(c, odd ? lds_a1 : lds_a0, odd ? lds_a0 : lds_a1);
+  }
+
+  // epilogue: lane holds rows 4 lq + i of each sub-tile, column lr
+  if (PHASE == kGateUp) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int col = tile * (kBN / 2) + wave * 32 + 16 * s + lr;
+      if (col >= p.I) continue;
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t tok = t0 + mi * 16 + 4 * lq + i;
+          if (tok >= p.T) continue;
+          const float hv = silu_mul(acc[mi][s][i], acc[mi][s + 2][i]);
+          p.h_shared[tok * p.I + col] = (uint16_t)(pack_bf16x2(hv, 0.f) & 0xFFFFu);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tok = t0 + mi * 16 + 4 * lq + i;
+        if (tok >= p.T) continue;
+        float* dst = p.y_shared + tok * p.N;
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s) {
+          const int col = tile * kBN + wave * 64 + 16 * s + lr;
+          if (col < p.N) dst[col] = acc[mi][s][i];
+        }
+      }
   }
 }
 
@@ -485,13 +854,33 @@ __device__ __forceinline__ void run_block(const GemmParams& p, int mblk, int til
   else block_tile<PHASE, kMaxMS, PK, MT>(p, mblk, tile, ntl);
 }
 
-// One work-group per (block, column tile). PK: the weights are in the
-// prepacked layout (a separate instance, so that traces tell the two apart).
+// The shared expert's work-groups: tile s % n_tiles of token block s / n_tiles
+// (consecutive work-groups share a token block, as the routed ones share a
+// bucket block).
+template <int PHASE>
+__device__ __forceinline__ void run_shared(const GemmParams& p, int sid, int n_tiles) {
+  const int tb = sid / n_tiles;
+  const int tile = sid - tb * n_tiles;
+  const int64_t t0 = (int64_t)tb * kBM;
+  const int64_t rows = p.T - t0 < kBM ? p.T - t0 : kBM;
+  if (rows <= 32) shared_tile<PHASE, 2>(p, t0, tile);
+  else if (rows <= 64) shared_tile<PHASE, 4>(p, t0, tile);
+  else shared_tile<PHASE, 6>(p, t0, tile);
+}
+
+// Shared-expert work-groups first (ids below n_shared), then one per
+// (block, column tile). PK: the weights are in the prepacked layout (a
+// separate instance, so that traces tell the two apart).
 template <int PHASE, bool PK>
-__global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p) {
-  const int n_tiles = p.N / tile_cols<PHASE>();
-  const int x = blockIdx.x % kXcds;
-  const int sx = blockIdx.x / kXcds;
+__global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p, int n_shared) {
+  const int n_tiles = (p.N + tile_cols<PHASE>() - 1) / tile_cols<PHASE>();
+  if ((int)blockIdx.x < n_shared) {
+    run_shared<PHASE>(p, blockIdx.x, n_tiles);
+    return;
+  }
+  const int id = blockIdx.x - n_shared;
+  const int x = id % kXcds;
+  const int sx = id / kXcds;
   const int mblk = (sx / n_tiles) * kXcds + x;
   const int tile = sx - (sx / n_tiles) * n_tiles;
   if (mblk >= p.max_blocks || (int64_t)mblk * kBM >= *p.n_padded) return;
@@ -505,10 +894,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gemm_kernel(GemmParams p)
 // ends with its stores alone. The grid holds one work-group per (block, tile);
 // the tiles per work-group are chosen from the real block count (the grid's
 // is an upper bound), as many as still leave six work-groups per CU, and the
-// work-groups past the last group exit at once.
+// work-groups past the last group exit at once. Whole tiles and an even chunk
+// count only.
 template <int PHASE, bool PK>
-__global__ __launch_bounds__(kThreads, 1) void prefill_tiles_kernel(GemmParams p, int tpw_max) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_tiles_kernel(GemmParams p, int n_shared,
+                                                                   int tpw_max) {
   const int n_tiles = p.N / tile_cols<PHASE>();
+  if ((int)blockIdx.x < n_shared) {
+    run_shared<PHASE>(p, blockIdx.x, n_tiles);
+    return;
+  }
+  const int id = blockIdx.x - n_shared;
   const int64_t nblk = *p.n_padded / kBM;
   int tpw = 1;
   for (int c = tpw_max; c > 1; c >>= 1)
@@ -517,8 +913,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_tiles_kernel(GemmParams p
       break;
     }
   const int ngrp = (n_tiles + tpw - 1) / tpw;  // groups of tpw consecutive tiles
-  const int x = blockIdx.x % kXcds;
-  const int sx = blockIdx.x / kXcds;
+  const int x = id % kXcds;
+  const int sx = id / kXcds;
   const int mblk = (sx / ngrp) * kXcds + x;
   const int tile = (sx - (sx / ngrp) * ngrp) * tpw;
   if (mblk >= p.max_blocks || (int64_t)mblk * kBM >= *p.n_padded) return;
@@ -527,30 +923,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_tiles_kernel(GemmParams p
 
 template <int PHASE>
 hipError_t launch(const GemmParams& p, hipStream_t stream) {
-  if (p.N % tile_cols<PHASE>() != 0 || p.K % (2 * kKC) != 0) return hipErrorInvalidValue;
+  if (p.K % kKC != 0) return hipErrorInvalidValue;
   // buffer resources hold 32-bit byte sizes
   const int64_t arows = PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM;
   const int64_t nw = PHASE == kGateUp ? 2 * (int64_t)p.I : p.N;
-  if (arows * p.K * 2 > 0x7fffffff || nw * p.K / 2 > 0x7fffffff) return hipErrorInvalidValue;
+  if (arows * p.K * 2 > 0x7fffffff || nw * p.K * 2 > 0x7fffffff || p.T * p.K * 2 > 0x7fffffff)
+    return hipErrorInvalidValue;
   const int64_t blocks = ((int64_t)p.max_blocks + kXcds - 1) / kXcds * kXcds;
-  const int n_tiles = p.N / tile_cols<PHASE>();
+  const int n_tiles = (p.N + tile_cols<PHASE>() - 1) / tile_cols<PHASE>();
   const int nch = p.K / kKC;
+  const int64_t n_shared64 = p.wshared ? (p.T + kBM - 1) / kBM * n_tiles : 0;
   // several tiles per work-group only where a tile is a few chunks long
-  // (at most 16 chunks per work-group, at most four tiles)
+  // (at most 16 chunks per work-group, at most four tiles), over whole tiles
+  // and an even chunk count
   int tpw = 1;
-  while (2 * tpw * nch <= 16 && 2 * tpw <= 4) tpw *= 2;
-  const int64_t grid = blocks * n_tiles;
+  if (p.N % tile_cols<PHASE>() == 0 && nch % 2 == 0)
+    while (2 * tpw * nch <= 16 && 2 * tpw <= 4) tpw *= 2;
+  const int64_t grid = n_shared64 + blocks * n_tiles;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   GemmParams args = p;
+  int n_shared = (int)n_shared64;
   if (tpw == 1) {
-    void* kargs[] = {&args};
+    void* kargs[] = {&args, &n_shared};
     const void* fn = p.prepacked
                          ? reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, true>)
                          : reinterpret_cast<const void*>(&prefill_gemm_kernel<PHASE, false>);
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
   }
-  void* kargs[] = {&args, &tpw};
+  void* kargs[] = {&args, &n_shared, &tpw};
   const void* fn = p.prepacked
                        ? reinterpret_cast<const void*>(&prefill_tiles_kernel<PHASE, true>)
                        : reinterpret_cast<const void*>(&prefill_tiles_kernel<PHASE, false>);
@@ -563,7 +964,15 @@ int32_t prefill_block_m() { return kBM; }
 
 bool prefill_fits(int32_t hidden, int32_t inter) {
   return inter % tile_cols<kGateUp>() == 0 && hidden % tile_cols<kDown>() == 0 &&
-         hidden % (2 * kKC) == 0 && inter % (2 * kKC) == 0;
+         hidden % kKC == 0 && inter % kKC == 0;
+}
+
+hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* kx, int64_t T, int32_t H,
+                      hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (H % 8 || T > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(x16_kernel, dim3((unsigned)T), dim3(kConvThreads), 0, stream, x, x16, kx, H);
+  return hipGetLastError();
 }
 
 hipError_t launch_gate_up_prefill(const GemmParams& p, hipStream_t stream) {

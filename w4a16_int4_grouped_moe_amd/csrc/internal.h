@@ -25,6 +25,8 @@ hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int
 struct GemmParams {
   // routed part
   const uint16_t* a_routed;     // gate_up: x [T, H]; down: h [rows, I] (sorted order)
+                                // (96-row blocks: fp16, scaled by 2^-a_exp)
+  const int32_t* a_exp;         // 96-row blocks: gate_up: kx [T]; down: kh [rows, n_htiles]
   const int32_t* sorted_ids;    // [max_blocks * bm]
   const int32_t* block_expert;  // [max_blocks]
   const int32_t* n_padded;      // [1]
@@ -36,6 +38,7 @@ struct GemmParams {
   const uint16_t* wshared;      // bf16 [Nw, K]
   // outputs
   uint16_t* h_routed;           // gate_up: h [max_blocks * bm, I]
+  int32_t* h_exp;               // 96-row blocks, gate_up: kh [max_blocks * bm, n_htiles]
   uint16_t* h_shared;           // gate_up: hs [T, I]
   float* y_routed;              // down: y [T*k, H], row = pair id
   float* y_shared;              // down: s [T, H]
@@ -46,6 +49,7 @@ struct GemmParams {
   int32_t K;                    // reduction width (H for gate_up, I for down)
   int32_t I;                    // intermediate width
   int32_t N;                    // output width (I for gate_up, H for down)
+  int32_t n_htiles;             // 96-row blocks: ceil(I / kHTile)
   uint32_t nibble_mask;         // 0x0F0F0F0F (a run-time value on purpose)
   int32_t prepacked;            // packed/scales in the prepacked layout (below)
 };
@@ -102,19 +106,24 @@ hipError_t launch_prepack(const int32_t* packed, const uint16_t* scales, int32_t
                           int32_t K, bool w13, int32_t I, uint8_t* codes_out,
                           uint8_t* scales_out, hipStream_t stream);
 
-hipError_t launch_gate_up(const GemmParams& p, int32_t block_m, hipStream_t stream);
-hipError_t launch_down(const GemmParams& p, int32_t block_m, hipStream_t stream);
-
 // Small-batch variants (buckets padded to 4 rows; see gemm_small.hip).
 // small_batch_fits: whether their staged scales fit in LDS for these widths.
 bool small_batch_fits(int32_t hidden, int32_t inter);
 hipError_t launch_gate_up_small(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_small(const GemmParams& p, hipStream_t stream);
 
-// Routed int4 experts in 96-row blocks (prefill-sized batches; see
-// gemm_prefill.hip). prefill_fits: whether the widths suit its tiles.
+// Routed int4 experts in 96-row blocks, with the bf16 shared expert's tiles
+// in the same launches (every batch past the small-batch regime; see
+// gemm_prefill.hip). Any hidden and inter that are multiples of 128;
+// prefill_fits: whether they are whole tiles (the prepacked layout needs it).
+// The routed products run in fp16: launch_x16 first converts x [T, H] (bf16)
+// into x16 (fp16, scaled per token by 2^-kx[t]); gate_up writes h in fp16
+// with one exponent per (row, kHTile columns).
+constexpr int32_t kHTile = 256;
 bool prefill_fits(int32_t hidden, int32_t inter);
 int32_t prefill_block_m();  // bucket rows per block of that path
+hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* kx, int64_t T, int32_t H,
+                      hipStream_t stream);
 hipError_t launch_gate_up_prefill(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream);
 
@@ -123,16 +132,6 @@ hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream);
 constexpr int32_t kMaxScored = 1024;  // scores per token (experts of the model)
 hipError_t launch_route(const float* scores, int64_t T, int32_t S, int32_t k, int32_t* topk_ids,
                         float* topk_weights, hipStream_t stream);
-// Dense bf16 GEMM of the shared expert (hipBLASLt; see shared_blas.cpp):
-// out [T, rows] fp32 = act [T, K] . weights [rows, K]^T, with
-// kSharedBlasWorkspace bytes of library workspace. hipErrorNotSupported when
-// the library offers no algorithm for the shape (nothing was launched).
-constexpr size_t kSharedBlasWorkspace = size_t(32) << 20;
-hipError_t launch_shared_blas(const uint16_t* weights, const uint16_t* act, float* out,
-                              int64_t rows, int64_t T, int64_t K, void* workspace,
-                              hipStream_t stream);
-// h [T, I] bf16 = silu(gu[:, :I]) * gu[:, I:] from fp32 gu [T, 2I].
-hipError_t launch_swiglu(const float* gu, uint16_t* h, int64_t T, int32_t I, hipStream_t stream);
 // out[t] = bf16(s[t] + sum_j valid * w[t,j] * y[t*k+j]), fp32 sum in slot order.
 hipError_t launch_combine(const float* y, const float* s, const int32_t* topk_ids,
                           const float* topk_weights, uint16_t* out, int64_t T, int32_t H,
