@@ -4,24 +4,29 @@
     python bench.py [--steps K] [--warmup W]
                     [--workload decode|prefill|skew|ep|tp8_decode|tp8_prefill|tiny]
 
-Default workload (the one the metric is quoted on): one Kimi-K2.6-shape MoE
-layer (hidden 7168, moe_intermediate 2048, 384 int4 group-32 experts, top-8,
-one bf16 shared expert) in decode, batches of 1, 8, 32 and 64 tokens. A step is
-one forward at each of the four batch sizes; every batch size has its own copy
-of the weights, so a call never finds weights left in L2/MALL by the previous
-call. Inputs are seeded synthetic data, resident in HBM before timing starts.
+Default (the metric "W4A16 MoE layer tokens/s; decode HBM GB/s and prefill
+TFLOP/s vs roofline"): one Kimi-K2.6-shape MoE layer (hidden 7168,
+moe_intermediate 2048, 384 int4 group-32 experts, top-8, one bf16 shared
+expert), timed in two legs:
 
-Prints one JSON line: tokens/s over the timed steps, the dominant kernel's
-roofline (algorithmic bytes or FLOPs per launch over its average duration,
-timed with HIP events that the library records around that kernel on its
-launch stream during the timed steps), the HBM traffic measured by rocprofv3
-counters when it was taken on the current kernel source, and the fp64 CPU
-oracle timed on a bounded sample of the same workload. `per_batch` adds a
-per-stage breakdown from a short pass with all stage events after the timed
-region (`us_per_call` there includes those extra event packets), and the time
-of the router step (scores -> top-k ids and weights) that would precede the
-layer, measured on its own (it is not part of the timed step: the layer takes
-ids and weights as inputs).
+  * decode (the headline `value`): a step is one forward at each of the batch
+    sizes 1, 8, 32 and 64 tokens; every batch size has its own copy of the
+    weights, so a call never finds weights left in L2/MALL by the previous
+    call. `roofline` is the HBM roofline of the routed experts' gate_up launch
+    (algorithmic bytes per launch over its average duration), `per_batch`
+    adds each batch's whole-layer HBM fraction;
+  * prefill (the `prefill` object): a step is one forward of 4096 tokens;
+    its `roofline` is the bf16/fp16 MFMA roofline of the gate_up launch
+    (routed experts and the shared expert: algorithmic FLOPs per launch over
+    its average duration).
+
+Inputs are seeded synthetic data, resident in HBM before timing starts. Launch
+durations come from HIP events that the library records around the launch on
+its own stream during the timed steps. `traffic` is the HBM traffic that
+rocprofv3 counters measured for the same kernel and workload, read from a
+record under profiles/ when that record was taken on the current kernel
+source (else null). `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -39,12 +44,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W4A16 MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s vs roofline"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-# block_m of the paths whose gate_up launch also carries the shared expert
-# (small-batch and tiled kernels); prefill-sized blocks give it its own launch
-SINGLE_LAUNCH_BLOCK_M = (4, 16, 64)
-GEMM_SRCS = [os.path.join(ROOT, "w4a16_int4_grouped_moe_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_small.hip", "gemm_prefill.hip")]
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / fp16 MFMA
+CSRC = os.path.join(ROOT, "w4a16_int4_grouped_moe_amd", "csrc")
+# the source of the gate_up kernel of each block size (traffic records are tied
+# to it)
+KERNEL_SRC = {4: "gemm_small.hip", 96: "gemm_prefill.hip"}
+KERNEL_NAME = {4: "small_gemm_kernel<gate_up>: routed + shared experts, int4 codes in a "
+                  "bf16 MFMA 4x4x4 with the fp32 group scale after it, fused SwiGLU",
+               96: "prefill_gemm_kernel<gate_up>: routed experts (exact fp16 dequantisation, "
+                   "MFMA 16x16x32 f16) + shared expert (MFMA 16x16x32 bf16), fused SwiGLU"}
 
 
 # ----------------------------------------------------------------------------
@@ -58,10 +66,9 @@ def w2_bytes(H, I):
     return H * I // 2 + H * (I // 32) * 2
 
 
-def work(T, H, I, k, ids, n_local, base, shared, shared_in_kernel=True):
-    """Bytes the layer must move and FLOPs it must do; gate_up_* are those of the
-    launch that carries the routed experts' gate_up (it also carries the shared
-    expert unless that runs in a launch of its own: shared_in_kernel False)."""
+def work(T, H, I, k, ids, n_local, base, shared):
+    """Bytes the layer must move and FLOPs it must do; gate_up_* are those of
+    the launch that carries the gate_up of the routed and shared experts."""
     import numpy as np
 
     flat = np.asarray(ids).ravel()
@@ -73,9 +80,8 @@ def work(T, H, I, k, ids, n_local, base, shared, shared_in_kernel=True):
     ts = T if shared else 0
     layer_bytes = U * (w13_bytes(H, I) + w2_bytes(H, I)) + s13 + s2 + 2 * T * H * 2 + T * k * 8
     layer_flops = (P + ts) * (2 * (2 * I) * H + 2 * H * I)
-    ks = ts if shared_in_kernel else 0
-    gate_up_bytes = U * w13_bytes(H, I) + (s13 if ks else 0) + T * H * 2 + (P + ks) * I * 2
-    gate_up_flops = (P + ks) * 2 * (2 * I) * H
+    gate_up_bytes = U * w13_bytes(H, I) + s13 + T * H * 2 + (P + ts) * I * 2
+    gate_up_flops = (P + ts) * 2 * (2 * I) * H
     return dict(P=P, U=U, gate_up_bytes=gate_up_bytes, layer_bytes=layer_bytes,
                 gate_up_flops=gate_up_flops, layer_flops=layer_flops)
 
@@ -89,7 +95,6 @@ class Hip:
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
-        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def event(self):
         e = ctypes.c_void_p()
@@ -102,24 +107,22 @@ class Hip:
         return ms.value
 
 
-def traffic_record(workload):
-    """rocprofv3 FETCH_SIZE / WRITE_SIZE of the gate_up kernel, if the record in
-    profiles/ was taken on the current GEMM sources (workload: the record's
-    name, e.g. "prefill" or "prefill_prepacked")."""
-    h = hashlib.sha256()
-    for f in GEMM_SRCS:
-        h.update(open(f, "rb").read())
-    sha = h.hexdigest()
-    path = os.path.join(ROOT, "profiles", f"gate_up_{workload}_traffic.md")
+def traffic_record(name, bm):
+    """rocprofv3 FETCH_SIZE / WRITE_SIZE of the gate_up kernel (record `name`,
+    e.g. "decode" or "prefill_prepacked"), if the record in profiles/ was
+    taken on the current source of that kernel."""
+    src = os.path.join(CSRC, KERNEL_SRC[bm])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    path = os.path.join(ROOT, "profiles", f"gate_up_{name}_traffic.md")
     if not os.path.exists(path):
-        return None
+        return None, path
     for line in open(path):
         m = re.match(r"\s*traffic_record:\s*(\{.*\})\s*$", line)
         if m:
             rec = json.loads(m.group(1))
-            if rec.get("gemm_sources_sha256") == sha:
-                return rec
-    return None
+            if rec.get("kernel_source_sha256") == sha:
+                return rec, path
+    return None, path
 
 
 def cpu_baseline(calls, shared, n_tokens, seconds):
@@ -156,6 +159,200 @@ def cpu_baseline(calls, shared, n_tokens, seconds):
                       f"{dt:.1f} s wall on {threads} threads"}
 
 
+STAGES = ["align+x16", "gate_up", "down", "combine"]
+
+
+class Leg:
+    """One workload: its batches (each with its own copy of the weights when
+    there are several), timed steps and per-stage diagnostics."""
+
+    def __init__(self, workload, batches, dev, prepacked=False):
+        import torch
+
+        import moe_inputs as mi
+        import w4a16_int4_grouped_moe_amd as moe
+
+        self.name = workload
+        self.batches = batches
+        self.prepacked = prepacked
+        w0 = mi.workload(workload, batches[0])
+        self.w0 = w0
+        g = self.g = w0.geo
+        bank = mi.device_bank(w0.seed_bank, g.hidden, g.inter, w0.bank_experts(), dev)
+        self.shared_np = mi.shared_weights(w0.seed_bank, g.hidden, g.inter) if g.shared else None
+        shared = mi.to_device(self.shared_np, dev) if g.shared else None
+        self.calls = []
+        for i, T in enumerate(batches):
+            w = mi.workload(workload, T)
+            x = mi.activations(w.seed_x + w.T, w.T, g.hidden)
+            ids, wts = mi.make_routing(w)
+            b = bank if i == 0 else {k: v.clone() for k, v in bank.items()}
+            s = shared if (i == 0 or shared is None) else shared.clone()
+            p = moe.problem(T, g.hidden, g.inter, w.n_local, g.top_k, w.expert_base)
+            c = dict(
+                w=w, T=T, x_np=x, ids_np=ids, wts_np=wts,
+                args=(mi.to_device(x, dev), mi.to_device(ids, dev), mi.to_device(wts, dev),
+                      b["packed_w13"], b["scales_w13"], b["packed_w2"], b["scales_w2"], s),
+                out=torch.empty((T, g.hidden), dtype=torch.bfloat16, device=dev),
+                ws=torch.empty(max(moe.workspace_size(p), 1), dtype=torch.uint8, device=dev),
+                work=work(T, g.hidden, g.inter, g.top_k, ids, w.n_local, w.expert_base, g.shared),
+                bm=moe.forward_block_m(p), base=w.expert_base)
+            if prepacked:  # the weight copy is replaced by its prepacked form
+                c["pk"] = moe.prepack(*c["args"][3:7])
+                c["args"] = c["args"][:3] + (None, None, None, None) + c["args"][7:]
+            self.calls.append(c)
+        torch.cuda.synchronize()
+
+    def run(self, c, events=None, pk=None):
+        import w4a16_int4_grouped_moe_amd as moe
+
+        x, ids, wts = c["args"][:3]
+        if pk is not None or self.prepacked:
+            moe.forward_prepacked(x, ids, wts, pk or c["pk"], c["args"][7], out=c["out"],
+                                  expert_base=c["base"], workspace=c["ws"], stage_events=events)
+        else:
+            moe.forward(*c["args"], out=c["out"], expert_base=c["base"], workspace=c["ws"],
+                        stage_events=events)
+
+    def time(self, hip, steps, warmup, pks=None):
+        """Warm-up, then `steps` timed steps (only the two events that bracket
+        the gate_up launch are recorded in them). Returns ms per step and the
+        gate_up launch durations (ms) per call and step."""
+        import torch
+
+        pks = pks or [None] * len(self.calls)
+        for _ in range(warmup):
+            for c, pk in zip(self.calls, pks):
+                self.run(c, pk=pk)
+        events = [[[None, hip.event(), None, None, None, hip.event(), None] for _ in self.calls]
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for step in range(steps):
+            for c, ev, pk in zip(self.calls, events[step], pks):
+                self.run(c, ev, pk)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        gu = [[hip.elapsed_ms(events[s][ci][1], events[s][ci][5]) for s in range(steps)]
+              for ci in range(len(self.calls))]
+        return ms, gu
+
+    def diag(self, hip, n):
+        """n more steps with all stage events (after the timed region): stage
+        durations (ms) per call, shape [call][step][stage], and the routed
+        launches' own durations."""
+        import torch
+
+        ev = [[[hip.event() for _ in range(7)] for _ in self.calls] for _ in range(n)]
+        for step in range(n):
+            for c, e in zip(self.calls, ev[step]):
+                self.run(c, e)
+        torch.cuda.synchronize()
+        st = [[[hip.elapsed_ms(ev[s][ci][j], ev[s][ci][j + 1]) for j in range(4)]
+               for s in range(n)] for ci in range(len(self.calls))]
+        gu = [[hip.elapsed_ms(ev[s][ci][1], ev[s][ci][5]) for s in range(n)]
+              for ci in range(len(self.calls))]
+        dn = [[hip.elapsed_ms(ev[s][ci][2], ev[s][ci][6]) for s in range(n)]
+              for ci in range(len(self.calls))]
+        return st, gu, dn
+
+    def record_name(self):
+        return self.name + ("_prepacked" if self.prepacked else "")
+
+
+def roofline(leg, gu_ms, bound):
+    """The gate_up launch against its roofline: per-launch algorithmic bytes
+    (hbm) or FLOPs (mfma) over its average duration in the timed steps."""
+    import numpy as np
+
+    mean_s = float(np.mean([np.mean(g) for g in gu_ms])) / 1e3
+    bm = leg.calls[0]["bm"]
+    rec, path = traffic_record(leg.record_name(), bm)
+    if bound == "mfma":
+        alg = float(np.mean([c["work"]["gate_up_flops"] for c in leg.calls]))
+        ach = alg / mean_s / 1e12
+        r = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(ach / MFMA_PEAK_TFLOPS, 4)}
+    else:
+        alg = float(np.mean([c["work"]["gate_up_bytes"] for c in leg.calls]))
+        ach = alg / mean_s / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4)}
+    r["traffic"] = (rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]) if rec else None
+    r["traffic_source"] = (
+        f"recorded: rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel and workload in "
+        f"{os.path.relpath(path, ROOT)}, taken on the current {KERNEL_SRC[bm]}" if rec else
+        f"no rocprofv3 record for the current {KERNEL_SRC[bm]} ({os.path.relpath(path, ROOT)})")
+    r["kernel"] = KERNEL_NAME[bm]
+    r["algorithmic_per_launch"] = alg
+    r["avg_launch_us"] = round(mean_s * 1e6, 2)
+    return r
+
+
+def per_batch(leg, st, gu_diag, dn_diag, gu_timed, route_us=None):
+    import numpy as np
+
+    out = []
+    for ci, c in enumerate(leg.calls):
+        s = np.array(st[ci])
+        call_s = float(np.median(s.sum(1))) / 1e3
+        wk = c["work"]
+        d = dict(
+            T=c["T"], us_per_call=round(call_s * 1e6, 2),
+            tokens_per_s=round(c["T"] / call_s, 1),
+            layer_hbm_gbs=round(wk["layer_bytes"] / call_s / 1e9, 1),
+            layer_hbm_frac=round(wk["layer_bytes"] / call_s / 1e9 / HBM_PEAK_GBS, 4),
+            layer_tflops=round(wk["layer_flops"] / call_s / 1e12, 2),
+            layer_mfma_frac=round(wk["layer_flops"] / call_s / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            experts_hit=wk["U"], pairs=wk["P"],
+            gate_up_us=round(float(np.mean(gu_timed[ci])) * 1e3, 2),
+            routed_us={"gate_up": round(float(np.mean(gu_diag[ci])) * 1e3, 2),
+                       "down": round(float(np.mean(dn_diag[ci])) * 1e3, 2)},
+            stage_us={n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, s.mean(0))})
+        if route_us is not None:
+            d["router_us"] = round(route_us[ci], 2)
+        out.append(d)
+    return out
+
+
+def router_times(leg, dev, n):
+    """The router step in front of the layer (scores of all the model's experts
+    -> top-k ids and weights), timed on its own per batch size."""
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import w4a16_int4_grouped_moe_amd as moe
+
+    g = leg.g
+    res = []
+    for c in leg.calls:
+        w = c["w"]
+        sc = torch.from_numpy(mi.router_scores(600 + w.T, w.T, g.n_experts)).to(dev)
+        rid = torch.empty((w.T, g.top_k), dtype=torch.int32, device=dev)
+        rw = torch.empty((w.T, g.top_k), dtype=torch.float32, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n + 1)]
+        for i in range(n + 1):
+            ev[i][0].record()
+            moe.route(sc, g.top_k, num_experts=w.n_local, expert_base=w.expert_base,
+                      topk_ids=rid, topk_weights=rw)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        res.append(float(np.median([a.elapsed_time(b) for a, b in ev[1:]])) * 1e3)
+    return res
+
+
+def describe(workload, batches, g):
+    if workload == "decode":
+        return ("Kimi-K2.6-shape W4A16 MoE layer decode: hidden 7168, moe_intermediate 2048, "
+                "384 int4 g32 experts, top-8, bf16 shared expert; batches 1/8/32/64 tokens")
+    if workload.startswith("tp8"):
+        return ("one GPU's share of the Kimi-K2.6-shape W4A16 MoE layer under 8-way tensor "
+                "parallelism: hidden 7168, moe_intermediate 256, 384 int4 g32 experts, top-8, "
+                f"bf16 shared expert (intermediate 256); batches {'/'.join(map(str, batches))}")
+    return f"Kimi-K2.6-shape W4A16 MoE layer, {workload} workload, T={batches[0]}"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,10 +363,12 @@ def main():
                              "tiny"])
     ap.add_argument("--tokens", type=int, default=0,
                     help="token count of a single-batch workload (default: the workload's own)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode workload only: skip the 4096-token prefill leg")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens per batch of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="wall time of the CPU-oracle sample (repeated passes)")
+                    help="wall time of each CPU-oracle sample (repeated passes)")
     ap.add_argument("--prepacked", action="store_true",
                     help="run the layer on prepacked weights (moe_w4a16_prepack, once per "
                          "weight copy, before the timed region)")
@@ -194,194 +393,38 @@ def main():
         batches = [1, 8, 32, 64]
     else:
         batches = [args.tokens or mi.workload(args.workload).T]
-    w0 = mi.workload(args.workload, batches[0])
-    g = w0.geo
+    hbm_bound = args.workload in ("decode", "tp8_decode", "skew", "ep", "tiny")
     t_setup = time.perf_counter()
-    bank = mi.device_bank(w0.seed_bank, g.hidden, g.inter, w0.bank_experts(), dev)
-    shared_np = mi.shared_weights(w0.seed_bank, g.hidden, g.inter) if g.shared else None
-    shared = mi.to_device(shared_np, dev) if g.shared else None
+    leg = Leg(args.workload, batches, dev, prepacked=args.prepacked)
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; workload {args.workload} "
+          f"batches {batches}", file=sys.stderr, flush=True)
 
-    calls = []
-    for i, T in enumerate(batches):
-        w = mi.workload(args.workload, T)
-        x = mi.activations(w.seed_x + w.T, w.T, g.hidden)
-        ids, wts = mi.make_routing(w)
-        b = bank if i == 0 else {k: v.clone() for k, v in bank.items()}
-        s = shared if (i == 0 or shared is None) else shared.clone()
-        p = moe.problem(T, g.hidden, g.inter, w.n_local, g.top_k, w.expert_base)
-        bm = moe.forward_block_m(p)
-        calls.append(dict(
-            w=w, T=T, x_np=x, ids_np=ids, wts_np=wts,
-            args=(mi.to_device(x, dev), mi.to_device(ids, dev), mi.to_device(wts, dev),
-                  b["packed_w13"], b["scales_w13"], b["packed_w2"], b["scales_w2"], s),
-            out=torch.empty((T, g.hidden), dtype=torch.bfloat16, device=dev),
-            ws=torch.empty(max(moe.workspace_size(p), 1), dtype=torch.uint8, device=dev),
-            work=work(T, g.hidden, g.inter, g.top_k, ids, w.n_local, w.expert_base, g.shared,
-                      shared_in_kernel=bm in SINGLE_LAUNCH_BLOCK_M),
-            bm=bm, base=w.expert_base))
-    torch.cuda.synchronize()
-    t_setup = time.perf_counter() - t_setup
-    print(f"[bench] setup {t_setup:.1f} s; workload {args.workload} batches {batches}",
+    ms_per_step, gu = leg.time(hip, args.steps, args.warmup)
+    value = sum(batches) / (ms_per_step / 1e3)
+    n_diag = min(5, args.steps)
+    st, gu_d, dn_d = leg.diag(hip, n_diag)
+    route_us = router_times(leg, dev, n_diag)
+    roof = roofline(leg, gu, "hbm" if hbm_bound else "mfma")
+    print(f"[bench] {args.workload}: {ms_per_step:.4f} ms/step, {value:.1f} tokens/s",
           file=sys.stderr, flush=True)
 
-    if args.prepacked:
-        for c in calls:  # the weight copies are replaced by their prepacked form
-            a = c["args"]
-            c["pk"] = moe.prepack(a[3], a[4], a[5], a[6])
-            c["args"] = a[:3] + (None, None, None, None) + a[7:]
-        torch.cuda.synchronize()
-
-    def run(c, events=None):
-        if args.prepacked:
-            x, ids, wts = c["args"][:3]
-            moe.forward_prepacked(x, ids, wts, c["pk"], c["args"][7], out=c["out"],
-                                  expert_base=c["base"], workspace=c["ws"], stage_events=events)
-        else:
-            moe.forward(*c["args"], out=c["out"], expert_base=c["base"], workspace=c["ws"],
-                        stage_events=events)
-
-    for _ in range(args.warmup):
-        for c in calls:
-            run(c)
-    torch.cuda.synchronize()
-
-    # timed region: only the two events that bracket the dominant kernel (the
-    # routed experts' gate_up launch) are recorded, so that event packets add
-    # little to the step time
-    events = [[[None, hip.event(), None, None, None, hip.event(), None] for _ in calls]
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for step in range(args.steps):
-        for c, ev in zip(calls, events[step]):
-            run(c, ev)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_step = sum(batches)
-    value = tokens_per_step / (ms_per_step / 1e3)
-
-    # after the timed region: a short pass with all stage events, for the
-    # per-stage breakdown (these extra event packets lengthen the calls a little)
-    n_diag = min(5, args.steps)
-    diag = [[[hip.event() for _ in range(7)] for _ in calls] for _ in range(n_diag)]
-    for step in range(n_diag):
-        for c, ev in zip(calls, diag[step]):
-            run(c, ev)
-    torch.cuda.synchronize()
-
-    # the router step in front of the layer (scores of all the model's experts
-    # -> top-k ids and weights), timed on its own per batch size: HIP events
-    # around single calls on the launch stream
-    route_us = []
-    for c in calls:
-        w = c["w"]
-        sc = torch.from_numpy(mi.router_scores(600 + w.T, w.T, g.n_experts)).to(dev)
-        rid = torch.empty((w.T, g.top_k), dtype=torch.int32, device=dev)
-        rw = torch.empty((w.T, g.top_k), dtype=torch.float32, device=dev)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_diag + 1)]
-        for i in range(n_diag + 1):
-            ev[i][0].record()
-            moe.route(sc, g.top_k, num_experts=w.n_local, expert_base=w.expert_base,
-                      topk_ids=rid, topk_weights=rw)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        route_us.append(float(np.median([a.elapsed_time(b) for a, b in ev[1:]])) * 1e3)
-
-    # the same steps with the weights in prepacked form (moe_w4a16_prepack, a
-    # one-time load step outside the timing), where the widths allow it; the
-    # headline above stays on the checkpoint-layout weights the layer's entry
-    # point takes
+    # the same steps on prepacked copies of the same weights (a one-time load
+    # step outside the timing), where the widths allow it; the headline stays
+    # on the checkpoint-layout weights the layer's entry point takes
     prepacked = None
     if not args.prepacked:
         try:
-            pks = [moe.prepack(*c["args"][3:7]) for c in calls]
+            pks = [moe.prepack(*c["args"][3:7]) for c in leg.calls]
         except (ValueError, moe.MoeError):
             pks = None
         if pks:
-            def run_pk(c, pk, ev=None):
-                x, ids, wts = c["args"][:3]
-                moe.forward_prepacked(x, ids, wts, pk, c["args"][7], out=c["out"],
-                                      expert_base=c["base"], workspace=c["ws"], stage_events=ev)
-
-            for _ in range(args.warmup):
-                for c, pk in zip(calls, pks):
-                    run_pk(c, pk)
-            ev_pk = [[[None, hip.event(), None, None, None, hip.event(), None] for _ in calls]
-                     for _ in range(args.steps)]
-            torch.cuda.synchronize()
-            t2 = time.perf_counter()
-            for step in range(args.steps):
-                for c, pk, ev in zip(calls, pks, ev_pk[step]):
-                    run_pk(c, pk, ev)
-            torch.cuda.synchronize()
-            ms_pk = (time.perf_counter() - t2) * 1e3 / args.steps
+            ms_pk, gu_pk = leg.time(hip, args.steps, args.warmup, pks)
             prepacked = {
-                "value": round(tokens_per_step / (ms_pk / 1e3), 1), "ms_per_step": round(ms_pk, 4),
-                "gate_up_us": [round(float(np.mean([hip.elapsed_ms(ev_pk[s][ci][1], ev_pk[s][ci][5])
-                                                    for s in range(args.steps)])) * 1e3, 2)
-                               for ci in range(len(calls))],
+                "value": round(sum(batches) / (ms_pk / 1e3), 1), "ms_per_step": round(ms_pk, 4),
+                "gate_up_us": [round(float(np.mean(g)) * 1e3, 2) for g in gu_pk],
                 "note": "same steps with the weights prepacked once (moe_w4a16_prepack) and "
                         "moe_w4a16_forward_prepacked; results identical bit for bit"}
             del pks
-
-    stage_names = ["align", "gate_up", "down", "combine"]
-    per_batch = []
-    gate_up_ms, gate_up_bytes, gate_up_flops = [], [], []
-    for ci, c in enumerate(calls):
-        gu = np.array([hip.elapsed_ms(events[s][ci][1], events[s][ci][5])
-                       for s in range(args.steps)])
-        st = np.array([[hip.elapsed_ms(diag[s][ci][j], diag[s][ci][j + 1]) for j in range(4)]
-                       for s in range(n_diag)])
-        call_ms = st.sum(1)
-        wk = c["work"]
-        avg = st.mean(0)
-        per_batch.append(dict(
-            T=c["T"], us_per_call=round(float(np.median(call_ms)) * 1e3, 2),
-            tokens_per_s=round(c["T"] / (float(np.median(call_ms)) / 1e3), 1),
-            layer_hbm_gbs=round(wk["layer_bytes"] / (float(np.median(call_ms)) / 1e3) / 1e9, 1),
-            layer_tflops=round(wk["layer_flops"] / (float(np.median(call_ms)) / 1e3) / 1e12, 2),
-            experts_hit=wk["U"], pairs=wk["P"],
-            gate_up_us=round(float(gu.mean()) * 1e3, 2),
-            routed_us={"gate_up": round(float(np.mean([hip.elapsed_ms(diag[s][ci][1], diag[s][ci][5])
-                                                       for s in range(n_diag)])) * 1e3, 2),
-                       "down": round(float(np.mean([hip.elapsed_ms(diag[s][ci][2], diag[s][ci][6])
-                                                    for s in range(n_diag)])) * 1e3, 2)},
-            stage_us={n: round(float(v) * 1e3, 2) for n, v in zip(stage_names, avg)},
-            router_us=round(route_us[ci], 2)))
-        gate_up_ms.append(float(gu.mean()))
-        gate_up_bytes.append(wk["gate_up_bytes"])
-        gate_up_flops.append(wk["gate_up_flops"])
-
-    # dominant kernel: the gate_up GEMM (two thirds of the routed weight bytes
-    # and of the FLOPs); per-launch averages over the timed steps
-    mean_s = float(np.mean(gate_up_ms)) / 1e3
-    rec = traffic_record(args.workload + ("_prepacked" if args.prepacked else ""))
-    traffic = None
-    if rec is not None:
-        traffic = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-    if args.workload in ("prefill", "tp8_prefill"):
-        ach = float(np.mean(gate_up_flops)) / mean_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    else:
-        ach = float(np.mean(gate_up_bytes)) / mean_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
-    bms = [moe.forward_block_m(moe.problem(T, g.hidden, g.inter, w0.n_local, g.top_k))
-           for T in batches]
-    if all(b == 4 for b in bms):
-        roof["kernel"] = ("small_gemm_kernel<gate_up>: routed + shared experts, int4 dequant + "
-                          "MFMA 4x4x4, fused SwiGLU")
-    elif all(b in SINGLE_LAUNCH_BLOCK_M for b in bms):
-        roof["kernel"] = ("grouped_gemm_kernel<gate_up>: routed + shared experts, int4 dequant + "
-                          "MFMA 16x16x32, fused SwiGLU")
-    else:
-        roof["kernel"] = ("prefill_gemm_kernel<gate_up>: routed experts, int4 dequant + "
-                          "MFMA 16x16x32, fused SwiGLU")
-    roof["algorithmic_per_launch"] = (float(np.mean(gate_up_flops)) if roof["bound"] == "mfma"
-                                      else float(np.mean(gate_up_bytes)))
-    roof["avg_launch_us"] = round(mean_s * 1e6, 2)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -389,34 +432,56 @@ def main():
         src.fill_(1.0)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
+
+    # prefill leg of the default run: 4096 tokens, one call per step
+    prefill = None
+    if args.workload == "decode" and not args.no_prefill:
+        t_setup = time.perf_counter()
+        pleg = Leg("prefill", [4096], dev, prepacked=args.prepacked)
+        print(f"[bench] prefill setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr,
+              flush=True)
+        ms_p, gu_p = pleg.time(hip, args.steps, args.warmup)
+        st_p, gu_pd, dn_pd = pleg.diag(hip, n_diag)
+        wk = pleg.calls[0]["work"]
+        prefill = {
+            "workload": describe("prefill", [4096], pleg.g), "T": 4096,
+            "ms_per_layer": round(ms_p, 4), "tokens_per_s": round(4096 / (ms_p / 1e3), 1),
+            "layer_tflops": round(wk["layer_flops"] / (ms_p / 1e3) / 1e12, 2),
+            "layer_mfma_frac": round(wk["layer_flops"] / (ms_p / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "layer_hbm_gbs": round(wk["layer_bytes"] / (ms_p / 1e3) / 1e9, 1),
+            "dtype": "routed products fp16 x fp16 (exact dequantised weights), shared expert "
+                     "bf16 x bf16, fp32 accumulation",
+            "roofline": roofline(pleg, gu_p, "mfma"),
+            "per_batch": per_batch(pleg, st_p, gu_pd, dn_pd, gu_p),
+        }
+        print(f"[bench] prefill: {ms_p:.4f} ms/layer", file=sys.stderr, flush=True)
+        if args.cpu_tokens > 0:
+            prefill["cpu_baseline"] = cpu_baseline(pleg.calls, pleg.shared_np,
+                                                   min(args.cpu_tokens, 16), args.cpu_seconds)
+        del pleg
 
     cpu = None
     if args.cpu_tokens > 0:
-        cpu = cpu_baseline(calls, shared_np, args.cpu_tokens, args.cpu_seconds)
+        cpu = cpu_baseline(leg.calls, leg.shared_np, args.cpu_tokens, args.cpu_seconds)
 
-    if args.workload == "decode":
-        wl = ("Kimi-K2.6-shape W4A16 MoE layer decode: hidden 7168, moe_intermediate 2048, "
-              "384 int4 g32 experts, top-8, bf16 shared expert; batches 1/8/32/64 tokens")
-    elif args.workload.startswith("tp8"):
-        wl = ("one GPU's share of the Kimi-K2.6-shape W4A16 MoE layer under 8-way tensor "
-              "parallelism: hidden 7168, moe_intermediate 256, 384 int4 g32 experts, top-8, "
-              f"bf16 shared expert (intermediate 256); batches {'/'.join(map(str, batches))}")
-    else:
-        wl = f"Kimi-K2.6-shape W4A16 MoE layer, {args.workload} workload, T={batches[0]}"
+    g = leg.g
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if leg.calls[0]["bm"] == 4 else "fp16 (routed) / bf16 (shared)",
         "data": "synthetic (seeded: int4 codes uniform, bf16 scales U(0.005,0.02), "
                 "x N(0,1), uniform distinct top-k routing, softmax weights)",
-        "config": {"workload": wl, "batches": batches, "hidden": g.hidden, "inter": g.inter,
+        "config": {"workload": describe(args.workload, batches, g), "batches": batches,
+                   "hidden": g.hidden, "inter": g.inter,
                    "weights": "prepacked" if args.prepacked else "checkpoint layout",
-                   "experts": w0.n_local, "top_k": g.top_k, "shared_expert": g.shared,
-                   "block_m": [moe.forward_block_m(moe.problem(T, g.hidden, g.inter, w0.n_local,
-                                                               g.top_k)) for T in batches]},
-        "per_batch": per_batch,
+                   "experts": leg.w0.n_local, "top_k": g.top_k, "shared_expert": g.shared,
+                   "block_m": [c["bm"] for c in leg.calls]},
+        "per_batch": per_batch(leg, st, gu_d, dn_d, gu, route_us),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "prepacked": prepacked,
     }
     print(json.dumps(line), flush=True)

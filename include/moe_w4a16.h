@@ -22,21 +22,28 @@
  *    "host". Every device pointer must be 16-byte aligned.
  *  - The caller allocates and owns every buffer, including the workspace, and
  *    keeps it alive until the stream work completes. The library allocates
- *    no buffers, keeps no pointer after it returns, never synchronises the
- *    host and launches only on `stream` (a hipStream_t; NULL is the null
- *    stream) on the current device. Calls that share a workspace must not
- *    overlap. One exception to "no allocation": prefill-sized calls (see
- *    moe_w4a16_forward_block_m: 96) run the bf16 shared expert's two dense
- *    GEMMs in hipBLASLt, whose handle is created on the first such call on a
- *    device and kept until the process ends (its plans are cached per shape);
- *    make one such call before capturing them into a HIP graph.
+ *    no buffers, keeps no state or pointer after it returns, never
+ *    synchronises the host and launches only on `stream` (a hipStream_t;
+ *    NULL is the null stream) on the current device, so every entry point may
+ *    be captured into a HIP graph at any time. Calls that share a workspace
+ *    must not overlap. Every kernel is this library's own HIP code.
  *  - Every argument error is detected on the host before any launch (so a
  *    failing call writes nothing) and reported as a negative status. Routing
  *    data on the device is never an error: ids outside [expert_base,
  *    expert_base + num_experts), -1 included, contribute nothing. NaNs
  *    propagate.
  *  - Limits: 1 <= top_k <= 16; 1 <= num_experts <= 512; hidden and inter
- *    multiples of 128; group_size == 32; num_tokens * top_k < 2^31 - 1.
+ *    multiples of 128 (a 128-input chunk is four whole quantisation groups,
+ *    and 16-byte loads then never straddle a row; every width of the model
+ *    family is one: 7168, 2048, and 256 per GPU of an 8-way tensor-parallel
+ *    split); group_size == 32; num_tokens * top_k < 2^31 - 1 (else
+ *    MOE_ERR_SHAPE). The kernels address each array through 32-bit buffer
+ *    descriptors, so a problem whose shared-expert matrix (2 * inter * hidden
+ *    bf16), or, past the decode regime, whose x (num_tokens * hidden bf16) or
+ *    bucketed intermediate rows (about (num_tokens * top_k + 95 *
+ *    num_experts) * inter * 2 bytes) would reach 2 GiB is refused with
+ *    MOE_ERR_UNSUPPORTED (at the Kimi-K2.6 shape: about 60,000 tokens per
+ *    call).
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H
@@ -144,11 +151,18 @@ int moe_w4a16_align_scratch_size(const moe_w4a16_problem *p, size_t *bytes);
  *   out          bf16  [T, H], fully overwritten; must not alias an input
  *   workspace    device scratch of at least moe_w4a16_workspace_size bytes
  *
- * Numerics: bf16 x bf16 matrix products with fp32 accumulation. The SwiGLU
- * output h is rounded to bf16 before the down product; the dequantised
- * weights are exact in the small-batch kernels (codes in the MFMA, scale
- * applied in fp32) and rounded to bf16 in the others; everything else stays
- * fp32 until the final bf16 rounding (round to nearest even).
+ * Numerics: the dequantised int4 weights (u - 8) * s are never rounded, and
+ * products accumulate in fp32. Decode-sized calls (moe_w4a16_forward_block_m
+ * 4) put the codes into bf16 MFMAs and multiply each group's fp32 scale
+ * after them, with h rounded to bf16. Larger calls (block_m 96) run the
+ * routed products in fp16, where (u - 8) * s is exact for bf16 group scales
+ * with 2^-17 <= |s| < 2^13 (smaller ones round to fp16's subnormal grid,
+ * larger ones overflow): x is converted once to fp16 with one power-of-two
+ * scale per token (exact down to 2^-32 of the token's largest |x|), and h is
+ * rounded once to fp16 with one power-of-two scale per row and 256 columns.
+ * The bf16 shared expert uses bf16 products with its h rounded to bf16.
+ * The routed and shared results are combined in fp32 and rounded once to
+ * bf16 (round to nearest even).
  */
 int moe_w4a16_forward(const void *x, const int32_t *topk_ids, const float *topk_weights,
                       const int32_t *packed_w13, const void *scales_w13,
@@ -161,11 +175,10 @@ int moe_w4a16_forward(const void *x, const int32_t *topk_ids, const float *topk_
  * addition records the caller's HIP events (hipEvent_t, created by the caller;
  * stage_events holds 7 entries, NULL entries are skipped) on `stream`:
  * [0] before the bucketing, [1] before the gate_up GEMM, [2] before the down
- * GEMM, [3] before the combine, [4] after it, [5] after the routed experts'
- * gate_up launch and [6] after the routed experts' down launch. Where the
- * shared expert runs in a launch of its own (prefill-sized blocks) it follows
- * [5] / [6]; elsewhere [5] / [6] directly follow the phase's single launch.
- * Used to time each kernel on its own stream.
+ * GEMM, [3] before the combine, [4] after it, [5] after the gate_up launch and
+ * [6] after the down launch (each launch carries the routed and the shared
+ * experts; with block_m 96 the conversion of x to fp16 runs between [0] and
+ * [1]). Used to time each kernel on its own stream.
  */
 int moe_w4a16_forward_timed(const void *x, const int32_t *topk_ids, const float *topk_weights,
                             const int32_t *packed_w13, const void *scales_w13,

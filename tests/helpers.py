@@ -35,3 +35,28 @@ def check(got_f64, ref, label=""):
     print(f"[parity] {label} {res}", flush=True)
     assert res["ok"], f"{label}: {res}"
     return res
+
+
+def block_edge_tokens(ids, expert_base, n_local, block_m):
+    """Tokens holding the first and the last row of every local expert's last
+    bucket block (rows of an expert are its valid pairs p = t*k + j in
+    ascending p, in blocks of block_m): together they reach every expert's
+    last block, including every overflow block past a full one."""
+    flat = np.asarray(ids).ravel()
+    k = np.asarray(ids).shape[1]
+    toks = set()
+    for e in range(n_local):
+        ps = np.nonzero(flat == expert_base + e)[0]
+        if ps.size == 0:
+            continue
+        toks.add(int(ps[-1] // k))
+        toks.add(int(ps[(ps.size - 1) // block_m * block_m] // k))
+    return sorted(toks)
+
+
+def sample_tokens(T, must, n_min, seed):
+    """`must` plus seeded random tokens up to n_min (sorted, distinct)."""
+    rest = np.setdiff1d(np.arange(T), np.asarray(must, np.int64))
+    extra = max(0, n_min - len(must))
+    pick = np.random.default_rng(seed).choice(rest, min(extra, rest.size), replace=False)
+    return np.sort(np.concatenate([np.asarray(must, np.int64), pick]))

@@ -7,7 +7,7 @@ import pytest
 
 import moe_inputs as mi
 import oracle
-from tests.helpers import check, oracle_rows, run_layer
+from tests.helpers import block_edge_tokens, check, oracle_rows, run_layer, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -127,21 +127,32 @@ def test_kimi_decode(dev, kimi, T):
     _kimi_case(dev, kimi, "decode", T)
 
 
-def test_kimi_prefill_sampled(dev, kimi):
-    _kimi_case(dev, kimi, "prefill", 4096, n_sample=10)
+def _edge_sample(name, T, n_min=256):
+    """At least n_min tokens of the workload, among them the first and last
+    rows of every local expert's last 96-row block."""
+    import w4a16_int4_grouped_moe_amd as moe
 
-
-def test_kimi_skew_sampled(dev, kimi):
-    w = mi.workload("skew", 512)
+    w = mi.workload(name, T)
     ids, _ = mi.make_routing(w)
-    hot = np.bincount(ids.ravel(), minlength=384).argmax()
-    hot_rows = np.nonzero((ids == hot).any(1))[0]
-    rows = np.unique(np.concatenate([hot_rows[:4], hot_rows[-2:], [0, 255, 511]]))
-    _kimi_case(dev, kimi, "skew", 512, rows=rows)
+    bm = moe.forward_block_m(moe.problem(T, w.geo.hidden, w.geo.inter, w.n_local, w.geo.top_k,
+                                         w.expert_base))
+    must = block_edge_tokens(ids, w.expert_base, w.n_local, bm)
+    return sample_tokens(T, must, n_min, seed=T)
+
+
+def test_kimi_prefill_sampled(dev, kimi):
+    # 4096 tokens: every expert's last block (about one in nine experts
+    # overflows its first 96-row block), ~400 tokens checked
+    _kimi_case(dev, kimi, "prefill", 4096, rows=_edge_sample("prefill", 4096))
+
+
+def test_kimi_skew_full(dev, kimi):
+    # all 512 tokens of the Zipf batch (hot experts span several blocks)
+    _kimi_case(dev, kimi, "skew", 512)
 
 
 def test_kimi_expert_parallel_share_sampled(dev, kimi):
-    _kimi_case(dev, kimi, "ep", 2048, n_sample=12)
+    _kimi_case(dev, kimi, "ep", 2048, rows=_edge_sample("ep", 2048))
 
 
 # ------------------------------------- 8-way tensor-parallel share (I = 256)
@@ -166,7 +177,7 @@ def test_tp8_share_prefill_sampled(dev, tp8):
     g = mi.TP8_SHARE
     print(f"[case] tp8_prefill block_m "
           f"{moe.forward_block_m(moe.problem(4096, g.hidden, g.inter, 384, 8, 0))}", flush=True)
-    _kimi_case(dev, tp8, "tp8_prefill", 4096, n_sample=12)
+    _kimi_case(dev, tp8, "tp8_prefill", 4096, rows=_edge_sample("tp8_prefill", 4096))
 
 
 def test_tp8_share_prefill_prepacked_bit_exact(dev, tp8):

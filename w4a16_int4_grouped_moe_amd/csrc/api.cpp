@@ -270,12 +270,13 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   int32_t* kx = reinterpret_cast<int32_t*>(ws + L.kx);
   int32_t* kh = reinterpret_cast<int32_t*>(ws + L.kh);
 
-  // gate_up + SwiGLU (96-row blocks: on x in fp16, converted first)
-  if ((err = mark(1)) != hipSuccess) return hip_status(err);
+  // gate_up + SwiGLU (96-row blocks: on x in fp16, converted with the
+  // bucketing's stage, before event 1)
   if (blocks96) {
     err = moe::launch_x16(static_cast<const uint16_t*>(x), x16, kx, T, H, strm);
     if (err != hipSuccess) return hip_status(err);
   }
+  if ((err = mark(1)) != hipSuccess) return hip_status(err);
   g.a_routed = blocks96 ? x16 : static_cast<const uint16_t*>(x);
   g.a_exp = kx;
   g.h_exp = kh;
