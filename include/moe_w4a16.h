@@ -276,6 +276,31 @@ int moe_w4a16_forward_prepacked_timed(const void *x, const int32_t *topk_ids,
                                       void *const *stage_events);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_w4a16_forward with the workspace taken from a device array inside the
+ * library instead of the caller. The array is MOE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB), one per GPU the library runs on, reserved with the library's code
+ * and held until the process ends; its address is looked up on the first call
+ * on each device (not a stream operation). Problems whose workspace
+ * (moe_w4a16_workspace_size) exceeds it get MOE_ERR_WORKSPACE before any
+ * launch: at the Kimi-K2.6 shape every decode batch up to 192 tokens fits.
+ * Every other argument and result as for moe_w4a16_forward (bit for bit).
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several threads without ordering) race, and
+ * the array keeps whatever the last call left there.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_w4a16_forward_noalloc(const void *x, const int32_t *topk_ids, const float *topk_weights,
+                              const int32_t *packed_w13, const void *scales_w13,
+                              const int32_t *packed_w2, const void *scales_w2,
+                              const void *shared_w, void *out, const moe_w4a16_problem *p,
+                              void *stream);
+
+/* The size of moe_w4a16_forward_noalloc's device array (host out). */
+int moe_w4a16_noalloc_workspace_limit(size_t *bytes);
+
+/*
  * A static description of `status`; for MOE_ERR_HIP it names the HIP error
  * of the failing call on this thread. Never NULL.
  */

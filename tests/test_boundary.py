@@ -33,6 +33,7 @@ def test_header_declares_expected_entry_points():
         "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_align_scratch_size",
         "moe_w4a16_forward",
         "moe_w4a16_forward_block_m", "moe_w4a16_forward_scores", "moe_w4a16_forward_timed",
+        "moe_w4a16_forward_noalloc", "moe_w4a16_noalloc_workspace_limit",
         "moe_w4a16_forward_prepacked", "moe_w4a16_forward_prepacked_timed",
         "moe_w4a16_prepack", "moe_w4a16_prepack_size",
         "moe_w4a16_route", "moe_w4a16_status_string", "moe_w4a16_workspace_size"])
@@ -301,3 +302,29 @@ def test_forward_prepacked_argument_errors_before_launch(lib):
     assert call(pp=P(num_experts=4, inter=384)) == moe.MOE_ERR_UNSUPPORTED
     # zero tokens: a no-op that touches no pointer
     assert call(b=None, x=None, pp=P(num_tokens=0, num_experts=4)) == moe.MOE_OK
+
+
+def test_noalloc_argument_errors_before_any_hip_call(lib):
+    """The allocation-free variant checks its arguments (and its array's size
+    limit) before resolving the array's address, so on a machine without a
+    GPU every argument error still comes back as its own status."""
+    good = [ctypes.c_void_p(0x10000 + 0x100 * i) for i in range(9)]
+    call = lambda ptrs, p: lib.moe_w4a16_forward_noalloc(*ptrs, ctypes.byref(p), None)
+    p = P(num_tokens=8)
+    for i in range(9):
+        if i == 7:
+            continue  # shared_w is optional
+        ptrs = list(good)
+        ptrs[i] = None
+        assert call(ptrs, p) == moe.MOE_ERR_NULL, i
+        ptrs[i] = ctypes.c_void_p(0x10008)
+        assert call(ptrs, p) == moe.MOE_ERR_ALIGNMENT, i
+    assert lib.moe_w4a16_forward_noalloc(*good, None, None) == moe.MOE_ERR_NULL
+    assert call(good, P(group_size=64)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(good, P(num_tokens=0)) == moe.MOE_OK
+    # past the array: 193 Kimi-shape tokens take 96-row blocks (> 64 MiB)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_w4a16_noalloc_workspace_limit(ctypes.byref(n)) == moe.MOE_OK
+    assert n.value == 64 << 20
+    assert moe.workspace_size(P(num_tokens=193)) > n.value
+    assert call(good, P(num_tokens=193)) == moe.MOE_ERR_WORKSPACE

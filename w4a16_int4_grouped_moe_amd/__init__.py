@@ -28,9 +28,11 @@ from ._binding import (  # noqa: F401
     align_scratch_size,
     forward,
     forward_block_m,
+    forward_noalloc,
     forward_prepacked,
     forward_scores,
     library,
+    noalloc_workspace_limit,
     prepack,
     prepack_size,
     problem,

@@ -72,12 +72,14 @@ def library():
                                                     [PP, P, ctypes.c_size_t, P])
         lib.moe_w4a16_forward_prepacked_timed.argtypes = (
             [P] * 3 + [P, ctypes.c_size_t, P, P] + [PP, P, ctypes.c_size_t, P, P])
+        lib.moe_w4a16_forward_noalloc.argtypes = [P] * 9 + [PP, P]
+        lib.moe_w4a16_noalloc_workspace_limit.argtypes = [ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_w4a16_status_string.argtypes = [ctypes.c_int]
         lib.moe_w4a16_status_string.restype = ctypes.c_char_p
         for f in ("workspace_size", "forward_block_m", "align_capacity", "align",
                   "align_scratch_size", "forward", "forward_timed", "route",
                   "forward_scores", "prepack_size", "prepack", "forward_prepacked",
-                  "forward_prepacked_timed"):
+                  "forward_prepacked_timed", "forward_noalloc", "noalloc_workspace_limit"):
             getattr(lib, "moe_w4a16_" + f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -230,6 +232,35 @@ def forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales
             raise ValueError("stage_events needs 7 entries")
         ev = (ctypes.c_void_p * 7)(*[e or None for e in stage_events])
         st = library().moe_w4a16_forward_timed(*args, ev)
+    _check(st)
+    return out
+
+
+def noalloc_workspace_limit() -> int:
+    """Bytes of the device array that forward_noalloc uses as its workspace."""
+    n = ctypes.c_size_t(0)
+    _check(library().moe_w4a16_noalloc_workspace_limit(ctypes.byref(n)))
+    return n.value
+
+
+def forward_noalloc(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+                    shared_w=None, out=None, expert_base: int = 0):
+    """forward with the library's own device array as the workspace
+    (moe_w4a16_forward_noalloc): nothing is allocated by the library; `out`
+    should be given by callers that cannot allocate. Calls that overlap on one
+    GPU race."""
+    torch = _torch()
+    _need(topk_ids, "topk_ids", torch.int32, 2, x.device)
+    k = topk_ids.shape[1]
+    # an empty placeholder: the workspace argument is not used
+    p, out, _ = _layer(x, k, packed_w13, scales_w13, packed_w2, scales_w2, shared_w, out,
+                       expert_base, torch.empty(0, dtype=torch.uint8, device=x.device))
+    _routing(topk_ids, topk_weights, x.shape[0], k, x.device)
+    st = library().moe_w4a16_forward_noalloc(
+        x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(), packed_w13.data_ptr(),
+        scales_w13.data_ptr(), packed_w2.data_ptr(), scales_w2.data_ptr(),
+        None if shared_w is None else shared_w.data_ptr(), out.data_ptr(), ctypes.byref(p),
+        _stream_handle(x.device))
     _check(st)
     return out
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe_w4a16.h"
 #include "internal.h"
 
@@ -184,20 +186,21 @@ int moe_w4a16_align(const int32_t* topk_ids, const moe_w4a16_problem* p, int32_t
                                       sorted_ids, block_expert, n_padded, (hipStream_t)stream));
 }
 
-// The layer call's argument checks (before any launch).
+// The layer call's argument checks (before any launch). own_workspace: the
+// workspace is the library's device array (not checked here).
 static int check_forward(const void* x, const int32_t* topk_ids, const float* topk_weights,
                          const int32_t* packed_w13, const void* scales_w13,
                          const int32_t* packed_w2, const void* scales_w2, const void* shared_w,
                          const void* out, const moe_w4a16_problem* p, const void* workspace,
-                         size_t workspace_bytes) {
+                         size_t workspace_bytes, bool own_workspace = false) {
   const int st = check_problem(p);
   if (st != MOE_OK) return st;
   if (p->num_tokens == 0) return MOE_OK;
   if (!x || !topk_ids || !topk_weights || !packed_w13 || !scales_w13 || !packed_w2 ||
-      !scales_w2 || !out || !workspace)
+      !scales_w2 || !out || (!workspace && !own_workspace))
     return MOE_ERR_NULL;
   const void* ptrs[] = {x, topk_ids, topk_weights, packed_w13, scales_w13,
-                        packed_w2, scales_w2, shared_w, out, workspace};
+                        packed_w2, scales_w2, shared_w, out, own_workspace ? nullptr : workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return MOE_ERR_ALIGNMENT;
   if (workspace_bytes < layout(p).total) return MOE_ERR_WORKSPACE;
@@ -321,6 +324,65 @@ int moe_w4a16_forward(const void* x, const int32_t* topk_ids, const float* topk_
                       size_t workspace_bytes, void* stream) {
   return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
                       shared_w, out, p, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free variant ------------------------------------------------
+// Its workspace is this file-scope device array (one per GPU, held until the
+// process ends). In host code `scratch` is only a host-side stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, once per device,
+// and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+// The address of the current device's scratch array (resolved on the first
+// call on that device, with the device current), or NULL with *err set.
+void* scratch_address(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int moe_w4a16_noalloc_workspace_limit(size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = MOE_NOALLOC_SCRATCH_BYTES;
+  return MOE_OK;
+}
+
+int moe_w4a16_forward_noalloc(const void* x, const int32_t* topk_ids, const float* topk_weights,
+                              const int32_t* packed_w13, const void* scales_w13,
+                              const int32_t* packed_w2, const void* scales_w2,
+                              const void* shared_w, void* out, const moe_w4a16_problem* p,
+                              void* stream) {
+  const int st = check_forward(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2,
+                               scales_w2, shared_w, out, p, nullptr,
+                               (size_t)MOE_NOALLOC_SCRATCH_BYTES, true);
+  if (st != MOE_OK || p->num_tokens == 0) return st;
+  hipError_t err = hipSuccess;
+  void* ws = scratch_address(&err);
+  if (!ws) return hip_status(err);
+  return forward_impl(x, topk_ids, topk_weights, packed_w13, scales_w13, packed_w2, scales_w2,
+                      shared_w, out, p, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_w4a16_forward_timed(const void* x, const int32_t* topk_ids, const float* topk_weights,
