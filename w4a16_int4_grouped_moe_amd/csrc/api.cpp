@@ -77,7 +77,7 @@ int32_t choose_block_m(const moe_w4a16_problem* p) {
 constexpr int64_t kAlignMultiMin = MOE_ALIGN_MULTI_MIN;
 
 struct Layout {
-  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, x16, kx, kh, total;
+  size_t sorted_ids, block_expert, meta, h, y, hs, s, align_scratch, x16, kx, kh, kr, total;
   int64_t cap_rows;
   int32_t max_blocks, bm, n_htiles;
 };
@@ -103,11 +103,12 @@ Layout layout(const moe_w4a16_problem* p) {
     o = round_up(o + 4 * (size_t)moe::align_scratch_ints((int64_t)P, p->num_experts));
   // 96-row blocks: x in fp16 with its per-token exponents, the per-(row,
   // tile) exponents of h
-  L.x16 = L.kx = L.kh = o;
+  L.x16 = L.kx = L.kh = L.kr = o;
   if (L.bm == moe::prefill_block_m()) {
     L.x16 = o; o = round_up(o + 2 * T * H);
     L.kx = o; o = round_up(o + 4 * T);
     L.kh = o; o = round_up(o + 4 * (size_t)L.cap_rows * L.n_htiles);
+    L.kr = o; o = round_up(o + 4 * (size_t)L.cap_rows);
   }
   L.total = o;
   return L;
@@ -272,6 +273,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.x16);
   int32_t* kx = reinterpret_cast<int32_t*>(ws + L.kx);
   int32_t* kh = reinterpret_cast<int32_t*>(ws + L.kh);
+  int32_t* kr = reinterpret_cast<int32_t*>(ws + L.kr);
 
   // gate_up + SwiGLU (96-row blocks: on x in fp16, converted with the
   // bucketing's stage, before event 1)
@@ -294,9 +296,13 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   err = gemm(g, true, 5);
   if (err != hipSuccess) return hip_status(err);
 
-  // down
+  // down (96-row blocks: h rows brought to one exponent per row first)
+  if (blocks96) {
+    err = moe::launch_h_rescale(h, kh, kr, n_padded, L.cap_rows, I, L.n_htiles, strm);
+    if (err != hipSuccess) return hip_status(err);
+  }
   g.a_routed = h;
-  g.a_exp = kh;
+  g.a_exp = kr;
   g.h_exp = nullptr;
   g.packed = packed_w2;
   g.scales = static_cast<const uint16_t*>(scales_w2);

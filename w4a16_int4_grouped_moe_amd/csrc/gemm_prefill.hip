@@ -20,9 +20,9 @@
 //    [2^14, 2^15)), which is exact for every value down to 2^-32 of the
 //    token's largest;
 //  * the SwiGLU output h is rounded once to fp16 with one power-of-two scale
-//    per (row, 256-column tile of gate_up), and the down launch rescales each
-//    tile to the row's largest scale while staging it (exact except values
-//    below 2^-38 of the row's largest);
+//    per (row, 256-column tile of gate_up); between the two launches
+//    h_rescale_kernel brings each row's tiles to the row's largest scale
+//    (exact except values below 2^-38 of the row's largest);
 //  * the accumulators are fp32; the scales come back in the epilogues (exact
 //    power-of-two multiplies).
 // The bf16 shared expert keeps bf16 operands (bf16 MFMA, x as given, its h
@@ -40,7 +40,6 @@
 //    the two 2-bit halves of its argument, so that the fragment reads (16 rows
 //    at one k offset per 16 lanes) are free of bank conflicts. gate_up copies
 //    them straight from HBM into LDS (buffer loads with an LDS destination);
-//    down loads its h rows into registers, rescales them and writes them;
 //  * weights: the 512 rows x 64 bytes (four groups of 32 codes) of the chunk,
 //    double buffered, the four groups of row r permuted by (r >> 1) & 3 for the
 //    same reason; lane (r = lane % 16, q = lane / 16) of a wave reads group q of
@@ -79,6 +78,13 @@ namespace {
 #define MOE_PREFILL_AUX 0
 #endif
 constexpr int kPrefillAux = MOE_PREFILL_AUX;
+// instruction scheduling of an MFMA step: 1 = activation reads, then one
+// MFMA per two VALU instructions; 2 = compiler's order within each step;
+// 0 = compiler's order across steps
+#ifndef MOE_PREFILL_SCHED
+#define MOE_PREFILL_SCHED 1
+#endif
+constexpr int kPrefillSched = MOE_PREFILL_SCHED;
 constexpr int kPrefillPackedAux = 2;
 
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
@@ -115,12 +121,21 @@ constexpr int kSharedAhead = 3;            // MFMA steps of shared weights in fl
 
 enum { kGateUp = 0, kDown = 1 };
 
+// the routed blocks' ring of four activation chunks (kBM rows x 128 inputs);
+// the shared-expert tiles use the first two as their double buffer. Each
+// buffer is an object of its own: the compiler then sees that a buffer load
+// into one (an LDS write it tracks with the vector-memory counter) does not
+// alias LDS reads of another, and does not wait for the copies just issued
+// before the next reads.
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kABytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kABytes];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_w0[kWBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_w1[kWBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_s0[kSBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t lds_s1[kSBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a2[kABytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a3[kABytes];
+// per wave: the bf16 scales of its 64 weight rows, 16 groups (four chunks)
+// per row, two buffers that alternate every four chunks
+constexpr int kScRow = 32;                   // bytes per row and period
+constexpr int kScBuf = 64 * kScRow;          // one wave's buffer
+__shared__ __attribute__((aligned(1024))) uint8_t lds_sc[kWaves][2][kScBuf];
 // per block row: the exponent of its activation scale (gate_up: the token's;
 // down: the row's largest h tile exponent), the h tile exponent being chosen,
 // and the per-wave maxima it is chosen from
@@ -283,9 +298,52 @@ __global__ __launch_bounds__(kConvThreads) void x16_kernel(const uint16_t* __res
   }
 }
 
+// ---- the h rescale between the launches ----------------------------------------
+// For every bucketed row r below n_padded: kr[r] = the largest of its tile
+// exponents kh[r][.], and each tile's fp16 values times 2^(kh - kr) in place
+// (a power of two <= 1: exact unless the value falls below fp16's range,
+// i.e. below 2^-38 of the row's largest). One work-group per row.
+__global__ __launch_bounds__(kConvThreads) void h_rescale_kernel(uint16_t* __restrict__ h,
+                                                                const int32_t* __restrict__ kh,
+                                                                int32_t* __restrict__ kr,
+                                                                const int32_t* __restrict__ n_padded,
+                                                                int I, int n_htiles) {
+  const int64_t r = blockIdx.x;
+  if (r >= *n_padded) return;
+  const int32_t* k = kh + r * n_htiles;
+  int m = k[0];
+  for (int j = 1; j < n_htiles; ++j) m = max(m, k[j]);
+  if (threadIdx.x == 0) kr[r] = m;
+  u32x4* row = reinterpret_cast<u32x4*>(h + r * I);
+  for (int g = threadIdx.x; g < I / 8; g += kConvThreads) {
+    const int d = k[g * 8 / kHTile] - m;
+    if (d == 0) continue;
+    // (the whole 16-byte piece is reinterpreted at once: a bit_cast of a
+    // single element of an ext_vector value miscompiles with this compiler,
+    // reading element 0 for every element)
+    const _Float16 f = (_Float16)__builtin_ldexpf(1.0f, d);
+    const h16x8 f8 = {f, f, f, f, f, f, f, f};
+    row[g] = __builtin_bit_cast(u32x4, __builtin_bit_cast(h16x8, row[g]) * f8);
+  }
+}
+
 // ---- routed int4 blocks ---------------------------------------------------------
-// MT: the work-group computes ntl consecutive column tiles of the block
-// (otherwise exactly one: ntl is then the constant 1)
+// K advances in chunks of 128 inputs (four groups of 32). Each wave streams
+// its own 64 weight rows straight into registers: lane (lr, lq) loads group
+// lq of row 16 s + lr of each sub-tile s (16 bytes; the four lanes of a row
+// read its 64 bytes of the chunk), three chunks ahead of their use, in a ring
+// of four register sets. The activations (kBM rows x 128 inputs) reach LDS
+// through buffer loads with an LDS destination, also three chunks ahead, in a
+// ring of four buffers. Each wave copies the bf16 scales of its rows into its
+// own LDS area, 16 groups (32 bytes) per row every four chunks. MFMA step j of
+// a chunk takes word j of every lane, so its 32-long reduction covers one
+// 8-input slice of each of the four groups; the matching activations are read
+// at piece 4 lq + j of each row. One barrier per chunk, which also frees the
+// activation buffer that the next copies overwrite. The down phase's
+// activations are the h rows in fp16 with one exponent per row
+// (h_rescale_kernel brings each row's tiles to its largest exponent between
+// the two launches).
+constexpr int kRing = 4;          // chunk slots in flight: the one computed + 3 ahead
 template <int PHASE, int MS, bool PK, bool MT>
 __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int tile, int ntl_arg) {
   const int ntl = MT ? ntl_arg : 1;
@@ -295,136 +353,52 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   const int lr = lane & 15;
   const int lq = lane >> 4;
   const int K = p.K;
-  const int nch = K / kKC;
+  const int nch = K / kKC;                   // 128-input chunks
+  const int nkp = (nch + kRing - 1) / kRing * kRing;  // chunk slots per tile
   const int64_t row0 = (int64_t)mblk * kBM;
   const int e = p.block_expert[mblk];
   const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
   const int64_t wbase = (int64_t)e * Nw;
 
-  // ---- activation chunk c of tile t ------------------------------------------
-  // gate_up: x16 rows gathered by pair, copied into LDS by buffer loads with an
-  // LDS destination; instruction t covers LDS rows 4t..4t+3.
-  constexpr int kACopies = kBM / 4;                        // per work-group
-  constexpr int kAPerWave = (kACopies + kWaves - 1) / kWaves;
-  // down: thread t loads piece t % 16 of rows t / 16 + 32 i into registers,
-  // rescales them to the row's largest h tile exponent and writes them.
-  constexpr int kARows = kBM * 16 / kThreads;
-  static_assert(kBM * 16 % kThreads == 0, "down staging rows per thread");
+  // ---- activation copies: instruction u covers LDS rows 4u..4u+3 ------------
+  constexpr int kACopies = kBM / 4;
+  constexpr int kAPW = kACopies / kWaves;
+  static_assert(kACopies % kWaves == 0, "activation copies per wave");
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a_routed, 0,
       (int)((PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM) * K * 2), kBufferFlags);
-  uint32_t aoff[PHASE == kGateUp ? kAPerWave : kARows];
-  int kref[kARows];
-  const int apiece = tid & 15, arow = tid >> 4;
-  if (PHASE == kGateUp) {
+  uint32_t aoff[kAPW];
 #pragma unroll
-    for (int i = 0; i < kAPerWave; ++i) {
-      const int t = kAPerWave * wave + i;
-      const int row = 4 * t + (lane >> 4);
-      const int piece = (lane & 15) ^ aslot(row & 15);
-      int64_t src = -1;
-      if (t < kACopies && row < MS * 16) {
+  for (int i = 0; i < kAPW; ++i) {
+    const int row = 4 * (kAPW * wave + i) + (lane >> 4);
+    const int piece = (lane & 15) ^ aslot(row & 15);
+    int64_t src = -1;
+    if (row < MS * 16) {
+      if (PHASE == kGateUp) {
         const int32_t pair = p.sorted_ids[row0 + row];
         if (pair < p.P) src = pair / p.k;
+      } else {
+        src = row0 + row;
       }
-      aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kARows; ++i) {
-      const int r = arow + 32 * i;
-      aoff[i] = r < MS * 16 ? (uint32_t)(((row0 + r) * K + apiece * 8) * 2) : kNoRow;
-      int m = -1000;
-      if (r < MS * 16) {
-        const int32_t* ke = p.a_exp + (row0 + r) * p.n_htiles;
-        for (int j = 0; j < p.n_htiles; ++j) m = max(m, ke[j]);
-      }
-      kref[i] = m;
-    }
+    aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
   }
-  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.a_exp, 0,
-      PHASE == kGateUp ? 0 : (int)((int64_t)p.max_blocks * kBM * p.n_htiles * 4), kBufferFlags);
-  u32x4 areg[kARows];
-  int kreg[kARows];
+  // slot c of tile t; past the tiles or the chunks, offsets past any buffer
+  // (zeros; the copies are issued all the same, so that every chunk waits on
+  // the same number of loads)
   auto copy_a = [&](uint8_t* dst, int t, int c) {
-    if (PHASE == kGateUp) {
-      const int so = uniform(t < ntl ? c * kKC * 2 : (int)kNoRow);
+    const int so = uniform(t < ntl && c < nch ? c * kKC * 2 : (int)kNoRow);
 #pragma unroll
-      for (int i = 0; i < kAPerWave; ++i) {
-        const int tt = kAPerWave * wave + i;
-        if (kACopies % kWaves == 0 || tt < kACopies)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + tt * 1024), 16, aoff[i],
-                                                   so, 0, 0);
-      }
-    } else {
-      // loads into registers; the h tile exponents of the chunk's rows with them
-      const int so = uniform(t < ntl ? c * kKC * 2 : (int)kNoRow);
-      const int ko = uniform(t < ntl ? (c * kKC / kHTile) * 4 : (int)kNoRow);
-#pragma unroll
-      for (int i = 0; i < kARows; ++i) {
-        areg[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[i], so, 0));
-        const int r = arow + 32 * i;
-        kreg[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(
-            kres, r < MS * 16 ? (uint32_t)((row0 + r) * p.n_htiles * 4) : kNoRow, ko, 0);
-      }
-    }
-  };
-  // down: the loaded pieces, rescaled by 2^(tile exponent - row exponent) <= 1,
-  // into LDS (after the loads have been waited for)
-  auto store_a = [&](uint8_t* dst) {
-    if (PHASE == kDown) {
-#pragma unroll
-      for (int i = 0; i < kARows; ++i) {
-        const int r = arow + 32 * i;
-        if (r < MS * 16) {
-          // (the whole 16-byte piece is reinterpreted at once: a bit_cast of
-          // a single element of an ext_vector value miscompiles with this
-          // compiler, reading element 0 for every element)
-          const _Float16 f = (_Float16)__builtin_ldexpf(1.0f, kreg[i] - kref[i]);
-          const h16x8 f8 = {f, f, f, f, f, f, f, f};
-          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_bit_cast(h16x8, areg[i]) * f8);
-          *reinterpret_cast<u32x4*>(dst + r * (kKC * 2) + ((apiece ^ aslot(r & 15)) * 16)) = v;
-        }
-      }
-    }
+    for (int i = 0; i < kAPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + (kAPW * wave + i) * 1024), 16,
+                                               aoff[i], so, 0, 0);
   };
 
-  // ---- weight copies: instruction u covers rows 16u..16u+15 (64 B each) ------
-  // Checkpoint layout: row R's 64 bytes of chunk ch at ch * 64 in its row of
-  // K / 2 bytes. Prepacked layout: the tile's chunk is one 32 KB run (rows of
-  // 64 bytes), so an instruction reads 1 KB of whole lines. Rows past the
-  // width read zeros.
+  // ---- weights into registers, scales into the wave's LDS area ---------------
   constexpr bool packed_layout = PK;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.packed + wbase * (K / 8)), 0, Nw * (K / 8) * 4, kBufferFlags);
-  uint32_t woff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = 16 * (4 * wave + i) + (lane >> 2);
-    const int g = (lane & 3) ^ wslot(R);
-    const int n = weight_row<PHASE>(p, tile, R);
-    woff[i] = n < 0 ? kNoRow
-              : packed_layout ? (uint32_t)(((tile * nch) * kBN + R) * kWRowBytes + 16 * g)
-                              : (uint32_t)((n * (K / 8) + 4 * g) * 4);
-  }
-  const int wstep = packed_layout ? kWBytes : kWRowBytes;  // bytes per chunk
-  // bytes from one tile's weights to the next tile's (whole tiles only)
-  const int wtile = packed_layout ? nch * kWBytes : tile_cols<PHASE>() * (K / 2);
-  auto copy_w = [&](uint8_t* dst, int t, int c) {
-    const int so = uniform(t < ntl ? t * wtile + c * wstep : (int)kNoRow);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(dst + (4 * wave + i) * 1024), 16,
-                                               woff[i], so, 0, PK ? kPrefillPackedAux : kPrefillAux);
-  };
-
-  // ---- scale copies: instruction v covers rows 32v..32v+31 (32 B each) -------
-  // (prepacked: a period of the tile is one 16 KB run; its periods are the
-  // four-chunk periods here)
-  static_assert(kSPeriod * kKC == 16 * 32, "scale periods of the prepacked layout");
-  const int nper = (nch + kSPeriod - 1) / kSPeriod;
+  const int nper = (nch + kSPeriod - 1) / kSPeriod;  // scale periods (4 chunks)
   const __amdgpu_buffer_rsrc_t sres =
       packed_layout
           ? __builtin_amdgcn_make_buffer_rsrc(
@@ -432,51 +406,61 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
                 0, (int)pack_scale_bytes(Nw, K), kBufferFlags)
           : __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + wbase * (K / 32)), 0,
                                               Nw * (K / 32) * 2, kBufferFlags);
-  uint32_t soff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int R = 32 * (2 * wave + i) + (lane >> 1);
-    const int n = weight_row<PHASE>(p, tile, R);
-    soff[i] = n < 0 ? kNoRow
-              : packed_layout ? (uint32_t)(((tile * nper) * kBN + R) * kSRowBytes + 16 * (lane & 1))
-                              : (uint32_t)((n * (K / 32) + 8 * (lane & 1)) * 2);
-  }
-  const int sstep = packed_layout ? kSBytes : kSRowBytes;  // bytes per period
-  const int stile = packed_layout ? nper * kSBytes : tile_cols<PHASE>() * (K / 16);
-  auto copy_s = [&](uint8_t* dst, int t, int lp) {
-    const int so = uniform(t < ntl ? t * stile + lp * sstep : (int)kNoRow);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_ptr)(dst + (2 * wave + i) * 1024), 16,
-                                               soff[i], so, 0, 0);
-  };
-
-  // ---- this lane's LDS read offsets -----------------------------------------
-  // weights: row R = 64 wave + 16 s + lr, group lq (permuted slot)
-  int wread[kNSub];
+  uint32_t woff[kNSub];
 #pragma unroll
   for (int s = 0; s < kNSub; ++s) {
     const int R = wave * 64 + 16 * s + lr;
-    wread[s] = R * kWRowBytes + (lq ^ wslot(R)) * 16;
+    const int n = weight_row<PHASE>(p, tile, R);
+    woff[s] = n < 0 ? kNoRow
+              : packed_layout ? (uint32_t)(((tile * nch) * kBN + R) * kWRowBytes + 16 * lq)
+                              : (uint32_t)(n * (K / 2) + 16 * lq);
   }
-  // scales: row R, group 4 (chunk % 4) + lq
-  const int sread = (wave * 64 + lr) * kSRowBytes + lq * 2;
-  constexpr int kACopyInstr = PHASE == kGateUp ? kAPerWave : 2 * kARows;
-  constexpr int kMaxCopies = kACopyInstr + 4 + 2;  // copy instructions per wave and chunk
-  // activations: row 16 mi + lr, piece 4 lq + j (permuted slot)
-  const int aread = lr * (kKC * 2);
+  // scales: instruction i of a period copies the 32 bytes (16 groups) of the
+  // wave's rows 32 i + lane / 2
+  uint32_t scoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int R = wave * 64 + 32 * i + (lane >> 1);
+    const int n = weight_row<PHASE>(p, tile, R);
+    scoff[i] = n < 0 ? kNoRow
+               : packed_layout ? (uint32_t)(((tile * nper) * kBN + R) * kSRowBytes + 16 * (lane & 1))
+                               : (uint32_t)(n * (K / 32) * 2 + 16 * (lane & 1));
+  }
+  // bytes from one tile's weights (scales) to the next tile's (whole tiles only)
+  const int wtile = packed_layout ? nch * kWBytes : tile_cols<PHASE>() * (K / 2);
+  const int stile = packed_layout ? nper * kSBytes : tile_cols<PHASE>() * (K / 16);
+  auto load_w = [&](u32x4 (&d)[kNSub], int t, int c) {
+    const int so = uniform(t < ntl && c < nch
+                               ? t * wtile + (packed_layout ? c * kWBytes : c * kWRowBytes)
+                               : (int)kNoRow);
+    const int aux = PK ? kPrefillPackedAux : kPrefillAux;
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s)
+      d[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], so, aux));
+  };
+  // the scales of period lp (chunks 4 lp .. 4 lp + 3) of tile t into buffer
+  // `par` (the parity of the period count across the tiles)
+  auto copy_sc = [&](int t, int lp, int par) {
+    const int so = uniform(t < ntl && lp < nper
+                               ? t * stile + (packed_layout ? lp * kSBytes : lp * kScRow)
+                               : (int)kNoRow);
+    uint8_t* dst = lds_sc[wave][par];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_ptr)(dst + i * 1024), 16, scoff[i], so,
+                                               0, 0);
+  };
 
-  // per-row activation exponents (gate_up: the token's; down: the row's
-  // largest h tile exponent), before the first barrier
+  // per-row activation exponents for the epilogue (gate_up: the token's;
+  // down: the row's, after h_rescale_kernel), made visible by the first
+  // barrier
   if (tid < kBM) {
     int v = 0;
     if (PHASE == kGateUp) {
       const int32_t pair = p.sorted_ids[row0 + tid];
       if (pair < p.P) v = p.a_exp[pair / p.k];
     } else if (tid < MS * 16) {
-      const int32_t* ke = p.a_exp + (row0 + tid) * p.n_htiles;
-      v = ke[0];
-      for (int j = 1; j < p.n_htiles; ++j) v = max(v, ke[j]);
+      v = p.a_exp[row0 + tid];
     }
     lds_rexp[tid] = v;
   }
@@ -487,102 +471,90 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // issue_copies() is called in the first MFMA step; the scheduler spreads its
-  // copy instructions between that step's MFMAs.
-  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], const h16x2 (&sc)[kNSub],
-                     auto&& issue_copies) {
-    h16x8 bw[2][kNSub];  // this step's and the next step's weights
+  // activations: row 16 mi + lr, piece 4 lq + j (permuted slot)
+  const int aread = lr * (kKC * 2);
+  // Four MFMA steps per chunk: the activation fragments are read first, then
+  // each sub-tile's weights are dequantised under the previous one's MFMAs.
+  // this lane's scales of a period, two bf16 per register: [sub-tile][chunk
+  // pair of the period]
+  uint32_t scr[kNSub][kSPeriod / 2];
+  auto read_sc = [&](int par) {
+    const uint8_t* sbuf = lds_sc[wave][par] + lr * kScRow + 2 * lq;
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) bw[0][s] = dequant8(w[s][0], sc[s]);
+    for (int s = 0; s < kNSub; ++s)
+#pragma unroll
+      for (int q = 0; q < kSPeriod; q += 2) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(sbuf + 16 * s * kScRow + 8 * q);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(sbuf + 16 * s * kScRow + 8 * q + 8);
+        scr[s][q / 2] = lo | (hi << 16);
+      }
+  };
+  auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], int q) {
+    h16x2 sc[kNSub];
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s)
+      sc[s] = scale_pair((q & 1) ? scr[s][q / 2] >> 16 : scr[s][q / 2] & 0xFFFFu);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       h16x8 a[MS];
-      const int apc = ((4 * lq + j) ^ aslot(lr)) * 16;  // inputs 32 lq + 8 j
+      const int apc = aread + (((4 * lq + j) ^ aslot(lr)) * 16);
 #pragma unroll
       for (int mi = 0; mi < MS; ++mi)
-        a[mi] = *reinterpret_cast<const h16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apc);
-      if (j < 3) {
+        a[mi] = *reinterpret_cast<const h16x8*>(abuf + mi * 16 * (kKC * 2) + apc);
 #pragma unroll
-        for (int s = 0; s < kNSub; ++s)
-          bw[(j + 1) & 1][s] = dequant8(w[s][j + 1], sc[s]);
+      for (int s = 0; s < kNSub; ++s) {
+        const h16x8 b = dequant8(w[s][j], sc[s]);
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi)
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], b, acc[mi][s], 0, 0, 0);
       }
+      if (kPrefillSched == 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 13, 0);  // VALU: first sub-tile's weights
 #pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-        for (int s = 0; s < kNSub; ++s)
-          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], bw[j & 1][s], acc[mi][s], 0, 0, 0);
-      if (j == 0) issue_copies();
-      // interleave: the activation reads first, then one MFMA per three VALU
-      // instructions of the next step's dequantisation, and in the first step
-      // one copy after each of the first MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
-#pragma unroll
-      for (int i = 0; i < MS * kNSub; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-        if (j == 0 && i < kMaxCopies) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        for (int i = 0; i < MS * kNSub; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (kPrefillSched == 2) {
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto read_scales = [&](h16x2 (&sc)[kNSub], int t, int c) {
-    const int per = t * nper + c / kSPeriod;  // period count across the tiles
-    const uint8_t* sb = (per & 1) ? lds_s1 : lds_s0;
-    const int g = (c % kSPeriod) * 8;  // bytes: 4 groups per chunk
-#pragma unroll
-    for (int s = 0; s < kNSub; ++s)
-      sc[s] = scale_pair(*reinterpret_cast<const uint16_t*>(sb + sread + s * 16 * kSRowBytes + g));
-  };
 
-  // The chunk's scales and this wave's weight words are read from LDS first;
-  // the weight buffer is then free (each wave copies and reads only its own
-  // rows), so the copy of chunk ch + 2 goes into it in this chunk: weights are
-  // fetched two chunks ahead, activations (shared by all waves, buffer freed
-  // by the barrier) one chunk ahead. The copies are issued between the first
-  // step's MFMAs, not as one burst after the barrier: a burst from all eight
-  // waves at once stalls them on issue with no MFMA work in flight.
-  auto chunk = [&](int t, int c, uint8_t* abuf, uint8_t* anext, uint8_t* wbuf) {
-    h16x2 sc[kNSub];
-    read_scales(sc, t, c);
-    u32x4 w[kNSub];
-#pragma unroll
-    for (int s = 0; s < kNSub; ++s) w[s] = *reinterpret_cast<const u32x4*>(wbuf + wread[s]);
-    wait_lgkm0();
+  // One chunk slot c (ring position q = c % 4): the copies and loads of slot
+  // c + 3 (ring position q - 1, freed by the previous barrier) are issued
+  // first, then slot c's MFMAs. Slot c + 1's loads must have landed before
+  // the barrier: every slot issues kAPW activation copies and kNSub weight
+  // loads, so at most the loads of the two slots after it may stay in
+  // flight. The scales of period p (slots 4p .. 4p + 3) are copied with the
+  // loads of slot 4p, issued in slot 4p - 3 (ring position 1): they have
+  // landed by the end of slot 4p - 1, and period p - 2, in the same buffer,
+  // was last read in slot 4p - 5. The two slots whose wait sees that copy
+  // among the last loads (ring positions 1 and 2) allow two more in flight.
+  constexpr int kSlotLoads = kAPW + kNSub;
+  // The ring position q = c % 4 is a compile-time constant at every call,
+  // and so is each activation buffer's identity (par: the parity of this
+  // slot's scale period; its scales are read into registers at q = 0, and the
+  // copy at q = 1 fills the other buffer).
+  auto chunk = [&](int t, int c, int q, int par, uint8_t* abuf, uint8_t* aprev,
+                   const u32x4 (&wcur)[kNSub], u32x4 (&wprev)[kNSub]) {
+    const int c3 = c + kRing - 1;
+    const int t3 = c3 < nkp ? t : t + 1, cc3 = c3 < nkp ? c3 : c3 - nkp;
+    if (q == 0) read_sc(par);
     __builtin_amdgcn_sched_barrier(0);
-    // the chunk after this one and the one after that (multi-tile work-groups
-    // have an even chunk count, so a tile boundary falls between two chunks of
-    // a pair)
-    const int t1 = c + 1 < nch ? t : t + 1, c1 = c + 1 < nch ? c + 1 : 0;
-    const int t2 = c + 2 < nch ? t : t + 1, c2 = c + 2 < nch ? c + 2 : c + 2 - nch;
-    // the next scale period, at the first chunk of each period
-    const int lp = c / kSPeriod;
-    const int tn = lp + 1 < nper ? t : t + 1, lpn = lp + 1 < nper ? lp + 1 : 0;
-    const bool new_s = c % kSPeriod == 0 && tn < ntl;
-    const int pbuf = (t * nper + lp + 1) & 1;
-    compute(abuf, w, sc, [&]() {
-      copy_a(anext, t1, c1);
-      copy_w(wbuf, t2, c2);
-      if (new_s) copy_s(pbuf ? lds_s1 : lds_s0, tn, lpn);
-    });
-    // activations and weights of chunk ch + 1 in LDS or registers (the copies
-    // of chunk ch + 2's weights and of the next scales may stay in flight);
-    // this chunk's LDS reads done before its activation buffer is overwritten
-    if (new_s) wait_vm<6>();
-    else wait_vm<4>();
-    store_a(anext);
+    if (q == 1) copy_sc(t3, cc3 / kSPeriod, par ^ 1);
+    copy_a(aprev, t3, cc3);
+    load_w(wprev, t3, cc3);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c < nch) compute(abuf, wcur, q);
+    if (q == 1 || q == 2) wait_vm<2 * kSlotLoads + 2>();
+    else wait_vm<2 * kSlotLoads>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
   };
 
-  // ---- pipeline -----------------------------------------------------------
-  copy_a(lds_a0, 0, 0);
-  copy_w(lds_w0, 0, 0);
-  copy_w(lds_w1, 0, 1);
-  copy_s(lds_s0, 0, 0);
-  wait_vm<0>();
-  store_a(lds_a0);
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();
   // ---- epilogue: lane holds rows 4 lq + i of each 16-row sub-tile, column lr
   auto epilogue = [&](int ctile) {
     if (PHASE == kGateUp) {
@@ -655,27 +627,33 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     }
   };
 
-  // one chunk per iteration, the buffers chosen by the chunk's parity (a
-  // body of two chunks plus an odd last one, three inlined copies, made the
-  // register allocator spill)
-  if (!MT) {
-    for (int c = 0; c < nch; ++c) {
-      const bool odd = c & 1;
-      chunk(0, c, odd ? lds_a1 : lds_a0, odd ? lds_a0 : lds_a1, odd ? lds_w1 : lds_w0);
-    }
-    epilogue(tile);
-    return;
-  }
-  // several tiles: they follow each other without a break in the copy
-  // stream (the last chunks of a tile already fetch the next tile's first
-  // ones); the accumulators restart at zero for each tile. The chunk count is
-  // even, so the parity of c is that of the chunk count so far.
+  // ---- pipeline -------------------------------------------------------------
+  // slots 0, 1, 2 (and the first scale period) in flight, slot 0 landed
+  u32x4 w0[kNSub], w1[kNSub], w2[kNSub], w3[kNSub];
+  copy_sc(0, 0, 0);
+  copy_a(lds_a0, 0, 0);
+  load_w(w0, 0, 0);
+  copy_a(lds_a1, 0, 1);
+  load_w(w1, 0, 1);
+  copy_a(lds_a2, 0, 2);
+  load_w(w2, 0, 2);
+  wait_vm<2 * kSlotLoads>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  // the ring's four positions in turn (whole rounds per tile); with several
+  // tiles the copy stream runs on from one tile into the next and the
+  // accumulators restart at zero for each tile
+  int par = 0;  // parity of the scale period count across the tiles
   for (int t = 0; t < ntl; ++t) {
-    for (int c = 0; c < nch; ++c) {
-      const bool odd = c & 1;
-      chunk(t, c, odd ? lds_a1 : lds_a0, odd ? lds_a0 : lds_a1, odd ? lds_w1 : lds_w0);
+    for (int c = 0; c < nkp; c += kRing) {
+      chunk(t, c, 0, par, lds_a0, lds_a3, w0, w3);
+      chunk(t, c + 1, 1, par, lds_a1, lds_a0, w1, w0);
+      chunk(t, c + 2, 2, par, lds_a2, lds_a1, w2, w1);
+      chunk(t, c + 3, 3, par, lds_a3, lds_a2, w3, w2);
+      par ^= 1;
     }
     epilogue(tile + t);
+    if (!MT) break;
 #pragma unroll
     for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
@@ -769,17 +747,19 @@ __device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int
       load_w(wring[(j + kSharedAhead) & 3], q + kSharedAhead);
       if (j < kSharedAhead) wait_vm<4 * kSharedAhead + kAPerWave>();
       else wait_vm<4 * kSharedAhead>();
-      bf16x8 a[MS];
-      const int apc = ((4 * lq + j) ^ aslot(lr)) * 16;
+      if (c < nch) {
+        bf16x8 a[MS];
+        const int apc = ((4 * lq + j) ^ aslot(lr)) * 16;
 #pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
-        a[mi] = *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apc);
+        for (int mi = 0; mi < MS; ++mi)
+          a[mi] = *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apc);
 #pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
+        for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
-        for (int s = 0; s < kNSub; ++s)
-          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], wring[j & 3][s], acc[mi][s],
-                                                               0, 0, 0);
+          for (int s = 0; s < kNSub; ++s)
+            acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], wring[j & 3][s],
+                                                                 acc[mi][s], 0, 0, 0);
+      }
     }
     // the activation copy of chunk c + 1 done (the weight loads of the next
     // kSharedAhead steps may stay in flight); this chunk's LDS reads done
@@ -788,9 +768,12 @@ __device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int
     __builtin_amdgcn_s_barrier();
   };
   static_assert(kSharedAhead + 1 == 4, "the weight ring has one slot per step of a chunk");
-  for (int c = 0; c < nch; ++c) {
-    const bool odd = c & 1;
-    chunk(c, odd ? lds_a1 : lds_a0, odd ? lds_a0 : lds_a1);
+  // pairs of chunks, so that each buffer is a compile-time choice (the compiler
+  // tells the two apart and does not wait for a copy into one before reading
+  // the other); a padding chunk past an odd count only keeps the loads even
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, lds_a0, lds_a1);
+    chunk(c + 1, lds_a1, lds_a0);
   }
 
   // epilogue: lane holds rows 4 lq + i of each sub-tile, column lr
@@ -972,6 +955,15 @@ hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* kx, int64_t T, 
   if (T == 0) return hipSuccess;
   if (H % 8 || T > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(x16_kernel, dim3((unsigned)T), dim3(kConvThreads), 0, stream, x, x16, kx, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_h_rescale(uint16_t* h, const int32_t* kh, int32_t* kr, const int32_t* n_padded,
+                            int64_t rows, int32_t I, int32_t n_htiles, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (I % 8 || rows > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(h_rescale_kernel, dim3((unsigned)rows), dim3(kConvThreads), 0, stream, h, kh,
+                     kr, n_padded, I, n_htiles);
   return hipGetLastError();
 }
 

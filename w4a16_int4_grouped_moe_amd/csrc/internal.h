@@ -26,7 +26,7 @@ struct GemmParams {
   // routed part
   const uint16_t* a_routed;     // gate_up: x [T, H]; down: h [rows, I] (sorted order)
                                 // (96-row blocks: fp16, scaled by 2^-a_exp)
-  const int32_t* a_exp;         // 96-row blocks: gate_up: kx [T]; down: kh [rows, n_htiles]
+  const int32_t* a_exp;         // 96-row blocks: gate_up: kx [T]; down: kr [rows]
   const int32_t* sorted_ids;    // [max_blocks * bm]
   const int32_t* block_expert;  // [max_blocks]
   const int32_t* n_padded;      // [1]
@@ -124,6 +124,10 @@ bool prefill_fits(int32_t hidden, int32_t inter);
 int32_t prefill_block_m();  // bucket rows per block of that path
 hipError_t launch_x16(const uint16_t* x, uint16_t* x16, int32_t* kx, int64_t T, int32_t H,
                       hipStream_t stream);
+// Between the launches: each bucketed row's h tiles rescaled to the row's
+// largest exponent kr[row] (rows below *n_padded of `rows`).
+hipError_t launch_h_rescale(uint16_t* h, const int32_t* kh, int32_t* kr, const int32_t* n_padded,
+                            int64_t rows, int32_t I, int32_t n_htiles, hipStream_t stream);
 hipError_t launch_gate_up_prefill(const GemmParams& p, hipStream_t stream);
 hipError_t launch_down_prefill(const GemmParams& p, hipStream_t stream);
 
