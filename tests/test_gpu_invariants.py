@@ -11,8 +11,11 @@ pytestmark = pytest.mark.gpu
 
 E, K = 16, 4
 # (tokens, hidden, inter): 96-row blocks on widths that are not whole tiles
-# (masked), 4-row blocks, and 96-row blocks on whole tiles
-SHAPES = {"masked": (96, 640, 384), "small-batch": (8, 512, 256), "prefill": (300, 512, 256)}
+# (masked), 4-row blocks (32 pairs: bucketed inside the GEMM launches, down
+# and combine in one; 16 tokens: the bucketing kernel and the combine kernel),
+# and 96-row blocks on whole tiles
+SHAPES = {"masked": (96, 640, 384), "small-batch": (8, 512, 256),
+          "small-batch-bucketed": (16, 512, 256), "prefill": (300, 512, 256)}
 
 
 @pytest.fixture(scope="module", params=sorted(SHAPES))
@@ -21,7 +24,8 @@ def setup(request):
     import w4a16_int4_grouped_moe_amd as moe
 
     T, H, I = SHAPES[request.param]
-    want = {"masked": 96, "small-batch": 4, "prefill": 96}[request.param]
+    want = {"masked": 96, "small-batch": 4, "small-batch-bucketed": 4,
+            "prefill": 96}[request.param]
     assert moe.forward_block_m(moe.problem(T, H, I, E, K)) == want
     dev = torch.device("cuda:0")
     bank = mi.weight_bank(3, H, I, list(range(E)))

@@ -3,6 +3,8 @@ edges: K not a multiple of the small-batch iteration (partial last
 iteration), down widths that take the narrow-K kernel (I = 128, 384), the
 streamed down kernel with several slice groups per work-group, the
 largest top-k (16) and expert count (512), expert bases with non-local ids,
+the decode launches that bucket the pairs themselves (at most 64 pairs and 8
+tokens) with their down-and-combine kernel's partial column slices,
 ragged token counts, both block sizes (4 and 96), and on the 96-row path
 widths that are not whole tiles (hidden % 512, inter % 256: masked column
 tiles) with an odd number of 128-input chunks.
@@ -28,6 +30,12 @@ CASES = [
     (1, 384, 128, 16, 16, 0, True, 4),     # top-16, narrow down (I = 128)
     (8, 256, 128, 512, 8, 0, True, 4),     # 512 local experts
     (120, 2048, 640, 128, 4, 0, True, 4),  # streamed down: 3 slice groups per work-group, last run of 2
+    # at most 64 pairs and 8 tokens: the launches bucket the pairs themselves
+    # and the down launch also combines
+    (4, 2176, 256, 8, 4, 0, True, 4),      # 3 row-sets per work-group, a partial last one
+    (8, 512, 256, 4, 2, 0, True, 4),       # four local experts of six
+    (4, 384, 128, 64, 16, 0, False, 4),    # 64 pairs on up to 64 experts, non-local ids
+    (6, 640, 1152, 12, 4, 3, True, 4),     # expert base, down K = 1152 (partial iteration)
     (33, 640, 384, 8, 4, 0, True, 96),     # 96-row blocks: masked tiles both phases, 5 / 3 chunks
     (97, 384, 640, 6, 2, 2, True, 96),     # masked tiles, 3 / 5 chunks, expert base
     (150, 1024, 512, 8, 2, 1, True, 96),   # whole tiles, expert base
@@ -71,3 +79,29 @@ def test_shape(dev, T, H, I, E, k, base, shared, bm):
                          bank.scales_w2, sw, base)
     res = check(mi.bf16_tensor_to_f64(out), ref, f"T={T} H={H} I={I} E={E} k={k} bm={bm}")
     assert res["max_small_err_over_rms"] <= 0.015, res
+
+
+def test_local_buckets_spanning_blocks(dev):
+    """The launches that bucket the pairs themselves (at most 64 pairs and 8
+    tokens), with buckets longer than one 4-row block: experts 0 and 1 take
+    six and eight pairs (two blocks each), an invalid id and a non-local one
+    drop their pairs."""
+    import torch
+
+    T, H, I, E, k = 8, 640, 384, 8, 2
+    ids = np.zeros((T, k), np.int32)
+    ids[:, 0] = 1
+    ids[:6, 1] = 0
+    ids[6, 1] = 5
+    ids[7, 1] = -1
+    ids[5, 0] = 9  # not a local expert
+    w = np.random.default_rng(7).uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    bank = mi.weight_bank(71, H, I, list(range(E)))
+    bank_dev = {kk: mi.to_device(v, dev) for kk, v in bank.__dict__.items()}
+    x = mi.activations(72, T, H)
+    sw = mi.shared_weights(73, H, I)
+    out = run_layer(dev, x, ids, w, bank_dev, sw)
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw, 0)
+    check(mi.bf16_tensor_to_f64(out), ref, "local buckets spanning blocks")

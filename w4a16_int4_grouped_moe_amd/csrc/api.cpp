@@ -239,7 +239,11 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   };
   hipError_t err = mark(0);
   if (err != hipSuccess) return hip_status(err);
-  if (T * k >= kAlignMultiMin)
+  // A few pairs: the gate_up launch buckets them itself (no bucketing launch).
+  const bool local = L.bm == 4 && T * k <= moe::kLocalPairs && T <= moe::kLocalTokens;
+  if (local)
+    err = hipSuccess;
+  else if (T * k >= kAlignMultiMin)
     err = moe::launch_align_multi(topk_ids, T * k, E, p->expert_base, L.bm, sorted, blk, n_padded,
                                   reinterpret_cast<int32_t*>(ws + L.align_scratch), strm);
   else
@@ -269,6 +273,13 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.nibble_mask = 0x0F0F0F0Fu;
   g.prepacked = prepacked ? 1 : 0;
   g.n_htiles = L.n_htiles;
+  g.local_route = local ? 1 : 0;
+  g.topk_ids = topk_ids;
+  g.n_experts = E;
+  g.expert_base = p->expert_base;
+  g.sorted_out = sorted;
+  g.block_expert_out = blk;
+  g.n_padded_out = n_padded;
   const bool blocks96 = L.bm == moe::prefill_block_m();
   uint16_t* x16 = reinterpret_cast<uint16_t*>(ws + L.x16);
   int32_t* kx = reinterpret_cast<int32_t*>(ws + L.kx);
@@ -295,6 +306,7 @@ static int forward_impl(const void* x, const int32_t* topk_ids, const float* top
   g.N = I;
   err = gemm(g, true, 5);
   if (err != hipSuccess) return hip_status(err);
+  g.local_route = 0;
 
   // down (96-row blocks: h rows brought to one exponent per row first)
   if (blocks96) {

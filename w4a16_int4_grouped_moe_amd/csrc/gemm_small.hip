@@ -134,15 +134,31 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Pairwise exchanges of lanes l and l ^ m: both lanes add the same two
+// rounded terms, so every lane of a class ends with bit-identical sums, and a
+// result's rounding does not depend on which lane (i.e. which bucket row) it
+// is read from. A rotation would add the terms in lane-dependent orders, and
+// an add contracted with the multiply before it (an FMA) would round one
+// lane's own term but not its partner's; hence no contraction here.
+__device__ __forceinline__ float add_xor4(float v) {  // ds_swizzle, xor mask 4
+#pragma clang fp contract(off)
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                   0x101F));
+}
+__device__ __forceinline__ float add_xor8(float v) {  // DPP row_ror:8 = xor 8 in a row
+#pragma clang fp contract(off)
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float add_xor(float v, int m) {  // m = 16 or 32
+#pragma clang fp contract(off)
+  return v + __shfl_xor(v, m);
+}
+
 // sum over the 16 k-parts: lanes with equal lane % 4
 __device__ __forceinline__ float kpart_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                     0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                     0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  v = add_xor8(add_xor4(v));
+  return add_xor(add_xor(v, 16), 32);
 }
 
 // Output columns per wave slice: gate_up slices cover 2*NR h columns (NR/2
@@ -545,6 +561,52 @@ __device__ __forceinline__ void small_tile(const GemmParams& p, int64_t row0, in
   }
 }
 
+// ---- local bucketing (decode path with at most kLocalPairs pairs) -----------
+// One wave buckets the pairs q < P (lane q holds pair q) in the align kernel's
+// order: local experts ascending, each bucket's pairs in ascending pair order,
+// padded with the sentinel P to a multiple of 4 rows. Every bucket holds a
+// pair, so there are at most P blocks and 4 P rows. sids (kLocalRows entries)
+// and bexp (kLocalPairs entries) are the caller's LDS arrays; returns the
+// block count (the same value in every lane).
+constexpr int kLocalRows = 4 * kLocalPairs;
+__device__ __forceinline__ int local_buckets(const int32_t* __restrict__ ids, int P, int E,
+                                             int base, int32_t* sids, int32_t* bexp) {
+  const int lane = threadIdx.x & 63;
+  int e = -1;
+  if (lane < P) {
+    const int v = ids[lane] - base;
+    e = (unsigned)v < (unsigned)E ? v : -1;
+  }
+  for (int r = lane; r < kLocalRows; r += 64) sids[r] = P;
+  // the pairs of this lane's expert: how many, and how many come before it
+  int cnt = 0, rank = 0;
+  for (int q = 0; q < P; ++q) {
+    const int eq = __builtin_amdgcn_readlane(e, q);
+    if (e >= 0 && eq == e) {
+      ++cnt;
+      rank += q < lane ? 1 : 0;
+    }
+  }
+  const int padded = (cnt + 3) & ~3;
+  const int lead = (e >= 0 && rank == 0) ? 1 : 0;  // first pair of its expert
+  // bucket start: the padded sizes of the smaller experts
+  int off = 0, total = 0;
+  for (int q = 0; q < P; ++q) {
+    if (__builtin_amdgcn_readlane(lead, q)) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      const int pq = __builtin_amdgcn_readlane(padded, q);
+      off += eq < e ? pq : 0;
+      total += pq;
+    }
+  }
+  // (a wave's LDS stores land in issue order: the positions overwrite the
+  // sentinels)
+  if (e >= 0) sids[off + rank] = lane;
+  if (lead)
+    for (int b = 0; b < padded / 4; ++b) bexp[off / 4 + b] = e;
+  return __builtin_amdgcn_readfirstlane(total) >> 2;
+}
+
 // One work-group = one block of rows x 4 consecutive wave slices, numbered
 // block-major (consecutive work-groups stream consecutive rows of one expert;
 // the default round-robin placement then spreads them over the XCDs). The
@@ -593,6 +655,36 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void small_gemm_kerne
     const int64_t b2 = bid - shared;
     const int64_t blk = b2 / wg_slices;
     const int s = (int)(b2 - blk * wg_slices);
+    // (local routing runs with at most kLocalTokens tokens, i.e. in the
+    // kTokBlocks instance)
+    static_assert(kLocalTokens <= 4 * kTokBlocks, "local routing instance");
+    if constexpr (PHASE == kGateUp && TB == kTokBlocks) {
+      if (p.local_route) {  // the work-group buckets the pairs itself
+        __shared__ int32_t lsids[kLocalRows];
+        __shared__ int32_t lbexp[kLocalPairs];
+        __shared__ int32_t lnb;
+        if (blk >= kLocalPairs) return;
+        const bool writer = blk == 0 && s == 0;
+        if (threadIdx.x < 64) {
+          const int nb = local_buckets(p.topk_ids, (int)p.P, p.n_experts, p.expert_base, lsids,
+                                       lbexp);
+          if (threadIdx.x == 0) lnb = nb;
+        }
+        __syncthreads();
+        const int nb = lnb;
+        if (writer) {  // the table for the down and combine launches
+          for (int i = threadIdx.x; i < 4 * nb; i += kThreads) p.sorted_out[i] = lsids[i];
+          for (int i = threadIdx.x; i < nb; i += kThreads) p.block_expert_out[i] = lbexp[i];
+          if (threadIdx.x == 0) *p.n_padded_out = 4 * nb;
+        }
+        if (blk >= nb) return;
+        GemmParams q = p;
+        q.sorted_ids = lsids;
+        q.block_expert = lbexp;
+        small_tile<PHASE, NR, true, 1, kSmallDepth, PK>(q, blk * 4, s * kWaves, lds);
+        return;
+      }
+    }
     if (blk * 4 >= *p.n_padded) return;
     small_tile<PHASE, NR, true, 1, kSmallDepth, PK>(p, blk * 4, s * kWaves, lds);
   }
@@ -871,12 +963,9 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(NR)) void stream_down_kern
 // ---------------------------------------------------------------------------
 template <int KG>
 __device__ __forceinline__ float kpart_sum_narrow(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                     0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                     0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-  if (KG >= 8) v += __shfl_xor(v, 16);
-  if (KG >= 16) v += __shfl_xor(v, 32);
+  v = add_xor8(add_xor4(v));
+  if (KG >= 8) v = add_xor(v, 16);
+  if (KG >= 16) v = add_xor(v, 32);
   return v;
 }
 

@@ -52,7 +52,24 @@ struct GemmParams {
   int32_t n_htiles;             // 96-row blocks: ceil(I / kHTile)
   uint32_t nibble_mask;         // 0x0F0F0F0F (a run-time value on purpose)
   int32_t prepacked;            // packed/scales in the prepacked layout (below)
+  // Small-batch gate_up with at most kLocalPairs pairs (local_route != 0):
+  // the work-groups bucket the pairs themselves
+  // from topk_ids (in the bucketing kernel's order; the input sorted_ids,
+  // block_expert and n_padded are not read), and one of them writes the
+  // bucketing to the *_out arrays for the launches that follow.
+  int32_t local_route;
+  const int32_t* topk_ids;      // [T, k]
+  int32_t n_experts;            // local experts
+  int32_t expert_base;          // global id of local expert 0
+  int32_t* sorted_out;          // [max_blocks * 4]
+  int32_t* block_expert_out;    // [max_blocks]
+  int32_t* n_padded_out;        // [1]
 };
+
+// (each routed work-group buckets all pairs before its first weight load:
+// worth it only while that is a few lane steps)
+constexpr int32_t kLocalPairs = 16;
+constexpr int32_t kLocalTokens = 8;  // tokens of the launch instance that does it
 
 // ---- prepacked weights ------------------------------------------------------
 // The layout moe_w4a16_prepack writes, per expert and matrix (W13: Nw = 2I
