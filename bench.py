@@ -14,7 +14,9 @@ expert), timed in two legs:
     weights, so a call never finds weights left in L2/MALL by the previous
     call. `roofline` is the HBM roofline of the routed experts' gate_up launch
     (algorithmic bytes per launch over its average duration), `per_batch`
-    adds each batch's whole-layer HBM fraction;
+    adds each batch's whole-layer time and HBM fraction (a call timed between
+    the library's first and last events, with none between its stages;
+    `stage_us_with_events` is a per-stage diagnostic whose events add gaps);
   * prefill (the `prefill` object): a step is one forward of 4096 tokens;
     its `roofline` is the bf16/fp16 MFMA roofline of the gate_up launch
     (routed experts and the shared expert: algorithmic FLOPs per launch over
@@ -237,6 +239,21 @@ class Leg:
               for ci in range(len(self.calls))]
         return ms, gu
 
+    def call_times(self, hip, n):
+        """n more steps with only the first and the last of the library's
+        events (no events between the stages, which would add gaps): each
+        batch's whole-call duration (ms) per step, shape [call][step]."""
+        import torch
+
+        ev = [[[hip.event(), None, None, None, hip.event(), None, None] for _ in self.calls]
+              for _ in range(n)]
+        for step in range(n):
+            for c, e in zip(self.calls, ev[step]):
+                self.run(c, e)
+        torch.cuda.synchronize()
+        return [[hip.elapsed_ms(ev[s][ci][0], ev[s][ci][4]) for s in range(n)]
+                for ci in range(len(self.calls))]
+
     def diag(self, hip, n):
         """n more steps with all stage events (after the timed region): stage
         durations (ms) per call, shape [call][step][stage], and the routed
@@ -289,13 +306,13 @@ def roofline(leg, gu_ms, bound):
     return r
 
 
-def per_batch(leg, st, gu_diag, dn_diag, gu_timed, route_us=None):
+def per_batch(leg, call_ms, st, gu_diag, dn_diag, gu_timed, route_us=None):
     import numpy as np
 
     out = []
     for ci, c in enumerate(leg.calls):
         s = np.array(st[ci])
-        call_s = float(np.median(s.sum(1))) / 1e3
+        call_s = float(np.median(call_ms[ci])) / 1e3
         wk = c["work"]
         d = dict(
             T=c["T"], us_per_call=round(call_s * 1e6, 2),
@@ -308,7 +325,7 @@ def per_batch(leg, st, gu_diag, dn_diag, gu_timed, route_us=None):
             gate_up_us=round(float(np.mean(gu_timed[ci])) * 1e3, 2),
             routed_us={"gate_up": round(float(np.mean(gu_diag[ci])) * 1e3, 2),
                        "down": round(float(np.mean(dn_diag[ci])) * 1e3, 2)},
-            stage_us={n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, s.mean(0))})
+            stage_us_with_events={n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, s.mean(0))})
         if route_us is not None:
             d["router_us"] = round(route_us[ci], 2)
         out.append(d)
@@ -402,6 +419,7 @@ def main():
     ms_per_step, gu = leg.time(hip, args.steps, args.warmup)
     value = sum(batches) / (ms_per_step / 1e3)
     n_diag = min(5, args.steps)
+    call_ms = leg.call_times(hip, max(n_diag, 10))
     st, gu_d, dn_d = leg.diag(hip, n_diag)
     route_us = router_times(leg, dev, n_diag)
     roof = roofline(leg, gu, "hbm" if hbm_bound else "mfma")
@@ -442,6 +460,7 @@ def main():
         print(f"[bench] prefill setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr,
               flush=True)
         ms_p, gu_p = pleg.time(hip, args.steps, args.warmup)
+        call_p = pleg.call_times(hip, n_diag)
         st_p, gu_pd, dn_pd = pleg.diag(hip, n_diag)
         wk = pleg.calls[0]["work"]
         prefill = {
@@ -453,7 +472,7 @@ def main():
             "dtype": "routed products fp16 x fp16 (exact dequantised weights), shared expert "
                      "bf16 x bf16, fp32 accumulation",
             "roofline": roofline(pleg, gu_p, "mfma"),
-            "per_batch": per_batch(pleg, st_p, gu_pd, dn_pd, gu_p),
+            "per_batch": per_batch(pleg, call_p, st_p, gu_pd, dn_pd, gu_p),
         }
         print(f"[bench] prefill: {ms_p:.4f} ms/layer", file=sys.stderr, flush=True)
         if args.cpu_tokens > 0:
@@ -478,7 +497,7 @@ def main():
                    "weights": "prepacked" if args.prepacked else "checkpoint layout",
                    "experts": leg.w0.n_local, "top_k": g.top_k, "shared_expert": g.shared,
                    "block_m": [c["bm"] for c in leg.calls]},
-        "per_batch": per_batch(leg, st, gu_d, dn_d, gu, route_us),
+        "per_batch": per_batch(leg, call_ms, st, gu_d, dn_d, gu, route_us),
         "roofline": roof,
         "cpu_baseline": cpu,
         "prefill": prefill,
