@@ -34,33 +34,32 @@
 // owns four 16-row weight sub-tiles (gate_up: two gate sub-tiles and the two
 // matching up sub-tiles) and computes them for all of the block's rows, so
 // each weight is dequantised exactly once per block. K advances in chunks of
-// 128 inputs (four 32-input groups):
-//  * activations: the kBM x 128 chunk, double buffered; a row's 16 pieces of 16
+// 128 inputs (four 32-input groups); a chunk's operands are requested three
+// chunks before its MFMAs:
+//  * activations: a ring of four kBM x 128 chunks in LDS, copied straight
+//    from HBM (buffer loads with an LDS destination); a row's 16 pieces of 16
 //    bytes are permuted, piece c of row r at slot c ^ f(r & 15) where f swaps
 //    the two 2-bit halves of its argument, so that the fragment reads (16 rows
-//    at one k offset per 16 lanes) are free of bank conflicts. gate_up copies
-//    them straight from HBM into LDS (buffer loads with an LDS destination);
-//  * weights: the 512 rows x 64 bytes (four groups of 32 codes) of the chunk,
-//    double buffered, the four groups of row r permuted by (r >> 1) & 3 for the
-//    same reason; lane (r = lane % 16, q = lane / 16) of a wave reads group q of
-//    row r of each of its sub-tiles;
-//    (both permutations measured free of bank conflicts on gfx950 16-byte LDS
-//    reads, where the simpler XOR forms are not)
-//  * scales: 16 groups (4 chunks) of each of the 512 rows, two buffers that
-//    alternate every 4 chunks;
+//    at one k offset per 16 lanes) are free of bank conflicts on gfx950
+//    16-byte LDS reads (the simpler XOR forms are not);
+//  * weights: no other wave reads a wave's weight rows, so they go straight
+//    to registers: lane (r = lane % 16, q = lane / 16) loads group q of row r
+//    of each of its four sub-tiles (16 bytes each), a ring of four chunks;
+//  * scales: per wave, 16 groups (four chunks) of each of its 64 rows, copied
+//    into LDS once per four chunks (two buffers that alternate), read into
+//    registers at the first chunk of each period;
 //  * the words are dequantised to fp16 (u - 8) * s and fed to the MFMA: step j
 //    of a chunk takes word j of every lane, so its 32-long reduction covers one
 //    8-input slice of each of the four groups; the matching activations are
-//    read at those offsets. The next step's dequantisation (VALU) is
-//    interleaved with this step's MFMAs.
-// One barrier per chunk: the copies of chunk c + 1 are issued during the first
-// MFMA step of chunk c and waited for after it. Barriers are raw s_barrier with
-// explicit waits (the fence of __syncthreads() would also wait for the copies
-// just issued). The number of 16-row sub-tiles holding bucket rows (even,
-// after rounding up) is a template parameter of the K loop, so the loop body
-// is straight-line code. Widths that are not whole tiles (hidden % 512,
-// inter % 256) run masked: weight rows past the width read zeros and their
-// outputs are not stored.
+//    read at those offsets. The dequantisation (VALU) is interleaved with the
+//    MFMAs.
+// One barrier per chunk, which also frees the activation slot that the next
+// copies overwrite. Barriers are raw s_barrier with explicit waits (the fence
+// of __syncthreads() would also wait for the copies just issued). The number
+// of 16-row sub-tiles holding bucket rows (even, after rounding up) is a
+// template parameter of the K loop, so the loop body is straight-line code.
+// Widths that are not whole tiles (hidden % 512, inter % 256) run masked:
+// weight rows past the width read zeros and their outputs are not stored.
 //
 // Shared-expert work-group: 96 tokens x 512 weight rows, activations through
 // LDS as above (bf16, rows = tokens), each wave streams its own bf16 weight
