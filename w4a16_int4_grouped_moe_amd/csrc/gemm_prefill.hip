@@ -131,10 +131,12 @@ __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kABytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a2[kABytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a3[kABytes];
 // per wave: the bf16 scales of its 64 weight rows, 16 groups (four chunks)
-// per row, two buffers that alternate every four chunks
+// per row; only the wave itself writes and reads its buffer (ordinary LDS
+// stores of registers: a copy with an LDS destination into it would make the
+// compiler wait for every copy in flight before reading it)
 constexpr int kScRow = 32;                   // bytes per row and period
 constexpr int kScBuf = 64 * kScRow;          // one wave's buffer
-__shared__ __attribute__((aligned(1024))) uint8_t lds_sc[kWaves][2][kScBuf];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_sc[kWaves][kScBuf];
 // per block row: the exponent of its activation scale (gate_up: the token's;
 // down: the row's largest h tile exponent), the h tile exponent being chosen,
 // and the per-wave maxima it is chosen from
@@ -437,17 +439,20 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     for (int s = 0; s < kNSub; ++s)
       d[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], so, aux));
   };
-  // the scales of period lp (chunks 4 lp .. 4 lp + 3) of tile t into buffer
-  // `par` (the parity of the period count across the tiles)
-  auto copy_sc = [&](int t, int lp, int par) {
+  // the scales of period lp (chunks 4 lp .. 4 lp + 3) of tile t: loaded
+  // into registers, then stored to the wave's LDS buffer
+  auto load_sc = [&](u32x4 (&r)[2], int t, int lp) {
     const int so = uniform(t < ntl && lp < nper
                                ? t * stile + (packed_layout ? lp * kSBytes : lp * kScRow)
                                : (int)kNoRow);
-    uint8_t* dst = lds_sc[wave][par];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_ptr)(dst + i * 1024), 16, scoff[i], so,
-                                               0, 0);
+      r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres, scoff[i], so, 0));
+  };
+  auto store_sc = [&](const u32x4 (&r)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(lds_sc[wave] + i * 1024 + lane * 16) = r[i];
   };
 
   // per-row activation exponents for the epilogue (gate_up: the token's;
@@ -477,8 +482,8 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // this lane's scales of a period, two bf16 per register: [sub-tile][chunk
   // pair of the period]
   uint32_t scr[kNSub][kSPeriod / 2];
-  auto read_sc = [&](int par) {
-    const uint8_t* sbuf = lds_sc[wave][par] + lr * kScRow + 2 * lq;
+  auto read_sc = [&]() {
+    const uint8_t* sbuf = lds_sc[wave] + lr * kScRow + 2 * lq;
 #pragma unroll
     for (int s = 0; s < kNSub; ++s)
 #pragma unroll
@@ -527,27 +532,29 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // first, then slot c's MFMAs. Slot c + 1's loads must have landed before
   // the barrier: every slot issues kAPW activation copies and kNSub weight
   // loads, so at most the loads of the two slots after it may stay in
-  // flight. The scales of period p (slots 4p .. 4p + 3) are copied with the
-  // loads of slot 4p, issued in slot 4p - 3 (ring position 1): they have
-  // landed by the end of slot 4p - 1, and period p - 2, in the same buffer,
-  // was last read in slot 4p - 5. The two slots whose wait sees that copy
-  // among the last loads (ring positions 1 and 2) allow two more in flight.
+  // flight. The scales of period p (slots 4p .. 4p + 3) are loaded into
+  // registers with the loads of slot 4p, issued in slot 4p - 3 (ring
+  // position 1), stored to the wave's LDS buffer in slot 4p - 1 (position 3),
+  // after the wave read period p - 1's scales from it in slot 4p - 4
+  // (position 0; a wave's LDS accesses are done in order), and read into
+  // registers in slot 4p. The two slots whose wait sees the scale loads among
+  // the last loads (positions 1 and 2) allow two more in flight.
   constexpr int kSlotLoads = kAPW + kNSub;
+  u32x4 sreg[2];  // the next period's scales, between positions 1 and 3
   // The ring position q = c % 4 is a compile-time constant at every call,
-  // and so is each activation buffer's identity (par: the parity of this
-  // slot's scale period; its scales are read into registers at q = 0, and the
-  // copy at q = 1 fills the other buffer).
-  auto chunk = [&](int t, int c, int q, int par, uint8_t* abuf, uint8_t* aprev,
+  // and so is each activation buffer's identity.
+  auto chunk = [&](int t, int c, int q, uint8_t* abuf, uint8_t* aprev,
                    const u32x4 (&wcur)[kNSub], u32x4 (&wprev)[kNSub]) {
     const int c3 = c + kRing - 1;
     const int t3 = c3 < nkp ? t : t + 1, cc3 = c3 < nkp ? c3 : c3 - nkp;
-    if (q == 0) read_sc(par);
+    if (q == 0) read_sc();
     __builtin_amdgcn_sched_barrier(0);
-    if (q == 1) copy_sc(t3, cc3 / kSPeriod, par ^ 1);
+    if (q == 1) load_sc(sreg, t3, cc3 / kSPeriod);
     copy_a(aprev, t3, cc3);
     load_w(wprev, t3, cc3);
     __builtin_amdgcn_sched_barrier(0);
     if (c < nch) compute(abuf, wcur, q);
+    if (q == 3) store_sc(sreg);
     if (q == 1 || q == 2) wait_vm<2 * kSlotLoads + 2>();
     else wait_vm<2 * kSlotLoads>();
     wait_lgkm0();
@@ -629,27 +636,26 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // ---- pipeline -------------------------------------------------------------
   // slots 0, 1, 2 (and the first scale period) in flight, slot 0 landed
   u32x4 w0[kNSub], w1[kNSub], w2[kNSub], w3[kNSub];
-  copy_sc(0, 0, 0);
+  load_sc(sreg, 0, 0);
   copy_a(lds_a0, 0, 0);
   load_w(w0, 0, 0);
   copy_a(lds_a1, 0, 1);
   load_w(w1, 0, 1);
   copy_a(lds_a2, 0, 2);
   load_w(w2, 0, 2);
+  store_sc(sreg);
   wait_vm<2 * kSlotLoads>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   // the ring's four positions in turn (whole rounds per tile); with several
   // tiles the copy stream runs on from one tile into the next and the
   // accumulators restart at zero for each tile
-  int par = 0;  // parity of the scale period count across the tiles
   for (int t = 0; t < ntl; ++t) {
     for (int c = 0; c < nkp; c += kRing) {
-      chunk(t, c, 0, par, lds_a0, lds_a3, w0, w3);
-      chunk(t, c + 1, 1, par, lds_a1, lds_a0, w1, w0);
-      chunk(t, c + 2, 2, par, lds_a2, lds_a1, w2, w1);
-      chunk(t, c + 3, 3, par, lds_a3, lds_a2, w3, w2);
-      par ^= 1;
+      chunk(t, c, 0, lds_a0, lds_a3, w0, w3);
+      chunk(t, c + 1, 1, lds_a1, lds_a0, w1, w0);
+      chunk(t, c + 2, 2, lds_a2, lds_a1, w2, w1);
+      chunk(t, c + 3, 3, lds_a3, lds_a2, w3, w2);
     }
     epilogue(tile + t);
     if (!MT) break;
