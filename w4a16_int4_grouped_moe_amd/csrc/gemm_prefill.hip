@@ -527,36 +527,57 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     }
   };
 
-  // One chunk slot c (ring position q = c % 4): the copies and loads of slot
-  // c + 3 (ring position q - 1, freed by the previous barrier) are issued
-  // first, then slot c's MFMAs. Slot c + 1's loads must have landed before
-  // the barrier: every slot issues kAPW activation copies and kNSub weight
-  // loads, so at most the loads of the two slots after it may stay in
-  // flight. The scales of period p (slots 4p .. 4p + 3) are loaded into
-  // registers with the loads of slot 4p, issued in slot 4p - 3 (ring
-  // position 1), stored to the wave's LDS buffer in slot 4p - 1 (position 3),
-  // after the wave read period p - 1's scales from it in slot 4p - 4
-  // (position 0; a wave's LDS accesses are done in order), and read into
-  // registers in slot 4p. The two slots whose wait sees the scale loads among
-  // the last loads (positions 1 and 2) allow two more in flight.
-  constexpr int kSlotLoads = kAPW + kNSub;
+  // One chunk slot c (ring position q = c % 4): the activation copies of
+  // slot c + 3 (into the LDS slot freed by the previous barrier) and, at even
+  // positions, the weights of slots c + 2 and c + 3 (into the two register
+  // stages of slots c - 2 and c - 1) are issued first, then slot c's MFMAs.
+  // Loading a pair of slots' weights together requests both 64-byte halves
+  // of each weight row's 128-byte line at once, so the line is fetched once
+  // (loaded a slot apart, the second half often found the line evicted).
+  // The scales of period p (slots 4p .. 4p + 3) are loaded into registers
+  // in slot 4p - 3 (position 1), stored to the wave's LDS buffer in slot
+  // 4p - 1 (position 3), after the wave read period p - 1's scales from it in
+  // slot 4p - 4 (position 0; a wave's LDS accesses are done in order), and
+  // read into registers in slot 4p.
+  // Loads issued per position (in this order): 0: weights 2 kNSub,
+  // activations kAPW; 1: scales 2, activations; 2: weights 2 kNSub,
+  // activations; 3: activations. Before the barrier of slot c, slot c + 1's
+  // weights and activations must have landed; the loads issued after the
+  // later of the two may stay in flight:
+  //   position 0: after slot c + 1's activations (issued at position 2):
+  //               kAPW + (2 kNSub + kAPW) = 14
+  //   position 1: after its weights (position 0): kNSub + kAPW + 2 + kAPW = 12
+  //   position 2: after its activations (position 0): 2 + kAPW + 2 kNSub + kAPW = 16
+  //   position 3: after its weights (position 2): kNSub + kAPW + kAPW = 10
+  static_assert(kAPW == 3 && kNSub == 4, "wait counts");
   u32x4 sreg[2];  // the next period's scales, between positions 1 and 3
   // The ring position q = c % 4 is a compile-time constant at every call,
   // and so is each activation buffer's identity.
   auto chunk = [&](int t, int c, int q, uint8_t* abuf, uint8_t* aprev,
-                   const u32x4 (&wcur)[kNSub], u32x4 (&wprev)[kNSub]) {
-    const int c3 = c + kRing - 1;
-    const int t3 = c3 < nkp ? t : t + 1, cc3 = c3 < nkp ? c3 : c3 - nkp;
+                   const u32x4 (&wcur)[kNSub], u32x4 (&wn2)[kNSub], u32x4 (&wn3)[kNSub]) {
+    auto next = [&](int d, int& tt, int& cc) {  // slot c + d as (tile, slot)
+      const int cd = c + d;
+      tt = cd < nkp ? t : t + 1;
+      cc = cd < nkp ? cd : cd - nkp;
+    };
+    int t2, c2, t3, c3;
+    next(2, t2, c2);
+    next(3, t3, c3);
     if (q == 0) read_sc();
     __builtin_amdgcn_sched_barrier(0);
-    if (q == 1) load_sc(sreg, t3, cc3 / kSPeriod);
-    copy_a(aprev, t3, cc3);
-    load_w(wprev, t3, cc3);
+    if (q == 1) load_sc(sreg, t3, c3 / kSPeriod);
+    if ((q & 1) == 0) {
+      load_w(wn2, t2, c2);
+      load_w(wn3, t3, c3);
+    }
+    copy_a(aprev, t3, c3);
     __builtin_amdgcn_sched_barrier(0);
     if (c < nch) compute(abuf, wcur, q);
     if (q == 3) store_sc(sreg);
-    if (q == 1 || q == 2) wait_vm<2 * kSlotLoads + 2>();
-    else wait_vm<2 * kSlotLoads>();
+    if (q == 0) wait_vm<14>();
+    else if (q == 1) wait_vm<12>();
+    else if (q == 2) wait_vm<16>();
+    else wait_vm<10>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
   };
@@ -636,15 +657,16 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // ---- pipeline -------------------------------------------------------------
   // slots 0, 1, 2 (and the first scale period) in flight, slot 0 landed
   u32x4 w0[kNSub], w1[kNSub], w2[kNSub], w3[kNSub];
+  // slot 0's and 1's weights, slots 0, 1 and 2's activations in flight, slot
+  // 0's landed (slots 1 and 2's activations may stay in flight)
   load_sc(sreg, 0, 0);
-  copy_a(lds_a0, 0, 0);
   load_w(w0, 0, 0);
-  copy_a(lds_a1, 0, 1);
   load_w(w1, 0, 1);
+  copy_a(lds_a0, 0, 0);
+  copy_a(lds_a1, 0, 1);
   copy_a(lds_a2, 0, 2);
-  load_w(w2, 0, 2);
   store_sc(sreg);
-  wait_vm<2 * kSlotLoads>();
+  wait_vm<2 * kAPW>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   // the ring's four positions in turn (whole rounds per tile); with several
@@ -652,10 +674,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   // accumulators restart at zero for each tile
   for (int t = 0; t < ntl; ++t) {
     for (int c = 0; c < nkp; c += kRing) {
-      chunk(t, c, 0, lds_a0, lds_a3, w0, w3);
-      chunk(t, c + 1, 1, lds_a1, lds_a0, w1, w0);
-      chunk(t, c + 2, 2, lds_a2, lds_a1, w2, w1);
-      chunk(t, c + 3, 3, lds_a3, lds_a2, w3, w2);
+      chunk(t, c, 0, lds_a0, lds_a3, w0, w2, w3);
+      chunk(t, c + 1, 1, lds_a1, lds_a0, w1, w2, w3);  // (no weight loads)
+      chunk(t, c + 2, 2, lds_a2, lds_a1, w2, w0, w1);
+      chunk(t, c + 3, 3, lds_a3, lds_a2, w3, w0, w1);  // (no weight loads)
     }
     epilogue(tile + t);
     if (!MT) break;
