@@ -116,17 +116,21 @@ constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 static_assert(kBN == kPackRows && kKC == kPackChunk, "tiles of the prepacked layout");
 static_assert(kHTile == kBN / 2, "h exponent tiles are the gate_up column tiles");
 constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
-constexpr int kSharedAhead = 3;            // MFMA steps of shared weights in flight
+constexpr int kSBM = kBM;                  // tokens per shared-expert work-group
+constexpr int kSKC = 64;                   // inputs per shared-expert stage
+constexpr int kSRow = kSKC * 2;            // bytes of a row per stage: one 128-byte line
 
 enum { kGateUp = 0, kDown = 1 };
 
 // the routed blocks' ring of four activation chunks (kBM rows x 128 inputs);
-// the shared-expert tiles use the first two as their double buffer. Each
-// buffer is an object of its own: the compiler then sees that a buffer load
-// into one (an LDS write it tracks with the vector-memory counter) does not
-// alias LDS reads of another, and does not wait for the copies just issued
-// before the next reads.
-__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kABytes];
+// the shared-expert tiles stage their weights in the first (sized for them)
+// and their activations in the next two. Each buffer is an object of its
+// own: the compiler then sees that a buffer load into one (an LDS write it
+// tracks with the vector-memory counter) does not alias LDS reads of
+// another, and does not wait for the copies just issued before the next
+// reads.
+constexpr int kSWBytes = kWaves * 64 * kSRow;  // shared-expert weight stage
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kSWBytes > kABytes ? kSWBytes : kABytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kABytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a2[kABytes];
 __shared__ __attribute__((aligned(1024))) uint8_t lds_a3[kABytes];
@@ -691,10 +695,19 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 // ---- shared-expert tiles (bf16 weights) -----------------------------------------
 // A work-group: 96 tokens (t0..) x 512 weight rows of the shared expert's
 // gate/up [2I, H] (gate_up; sub-tiles as in the routed blocks) or down [H, I].
-// Activations (x or the shared h, bf16) through LDS as in the routed blocks;
-// every lane loads, per MFMA step and sub-tile, the 16 bytes of its weight row
-// at inputs 32 lq + 8 j of the chunk (the fragment the routed layout reads at
-// that step), kSharedAhead steps ahead of their use.
+// Both operands go through LDS in stages of 64 inputs, one 128-byte line per
+// row: the activations (x or the shared h, bf16, 12 KB, two buffers) and the
+// weights (64 KB, one buffer; each wave copies and reads only its own 64
+// rows). Every copy instruction covers 8 rows x 128 bytes, whole lines: a
+// load that takes half of each line it touches runs at a quarter of the
+// rate. A lane copies the 16-byte piece p ^ sw(r) of row r into slot p
+// (sw(r) = (r >> 1) & 7), so that the fragment reads (16 rows at one piece)
+// fall in distinct banks. Per stage: the activation copies of the next stage
+// (into the other buffer) after the barrier, the wave's weight fragments,
+// then its weight copies of the next stage (they run under the activation
+// reads, the MFMAs and the next barrier), the activation fragments, the MFMAs.
+__device__ __forceinline__ int sswz(int r) { return (r >> 1) & 7; }
+
 template <int PHASE, int MS>
 __device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int tile) {
   const int tid = threadIdx.x;
@@ -703,51 +716,53 @@ __device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int
   const int lr = lane & 15;
   const int lq = lane >> 4;
   const int K = p.K;
-  const int nch = K / kKC;
-  const int nsteps = 4 * nch;
+  const int nst = K / kSKC;  // even: K is a multiple of 128
   const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
 
-  constexpr int kACopies = kBM / 4;
+  // activations: copy i (rows 8 i ..) by wave i % 8
+  constexpr int kACopies = 2 * MS;
   constexpr int kAPerWave = (kACopies + kWaves - 1) / kWaves;
   const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a_shared, 0, (int)(p.T * K * 2), kBufferFlags);
   uint32_t aoff[kAPerWave];
 #pragma unroll
-  for (int i = 0; i < kAPerWave; ++i) {
-    const int t = kAPerWave * wave + i;
-    const int row = 4 * t + (lane >> 4);
-    const int piece = (lane & 15) ^ aslot(row & 15);
+  for (int u = 0; u < kAPerWave; ++u) {
+    const int i = wave + kWaves * u;
+    const int row = 8 * i + (lane >> 3);
     const int64_t tok = t0 + row;
-    aoff[i] = (t < kACopies && row < MS * 16 && tok < p.T) ? (uint32_t)((tok * K + piece * 8) * 2)
-                                                            : kNoRow;
+    aoff[u] = (i < kACopies && tok < p.T)
+                  ? (uint32_t)((tok * K + 8 * ((lane & 7) ^ sswz(row))) * 2)
+                  : kNoRow;
   }
-  auto copy_a = [&](uint8_t* dst, int c) {
-    const int so = uniform(c < nch ? c * kKC * 2 : (int)kNoRow);
+  // weights: the wave's 64 rows, copy i covers rows 8 i ..
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
+  uint32_t woff[8];
 #pragma unroll
-    for (int i = 0; i < kAPerWave; ++i) {
-      const int tt = kAPerWave * wave + i;
-      if (kACopies % kWaves == 0 || tt < kACopies)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + tt * 1024), 16, aoff[i], so,
+  for (int i = 0; i < 8; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const int n = weight_row<PHASE>(p, tile, wave * 64 + row);
+    woff[i] = n < 0 ? kNoRow : (uint32_t)((n * K + 8 * ((lane & 7) ^ sswz(row))) * 2);
+  }
+  static_assert(kABytes >= kSBM * kSRow, "activation stage");
+  uint8_t* const wbuf = lds_a0 + wave * (64 * kSRow);
+  auto copy_a = [&](uint8_t* abuf, int st) {
+    const int so = uniform(st * kSRow);
+#pragma unroll
+    for (int u = 0; u < kAPerWave; ++u) {
+      const int i = wave + kWaves * u;
+      if (kACopies % kWaves == 0 || i < kACopies)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(abuf + i * 1024), 16, aoff[u], so,
                                                  0, 0);
     }
   };
-  const __amdgpu_buffer_rsrc_t wres =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.wshared, 0, Nw * K * 2, kBufferFlags);
-  uint32_t woff[kNSub];
+  auto copy_w = [&](int st) {
+    const int so = uniform(st * kSRow);
 #pragma unroll
-  for (int s = 0; s < kNSub; ++s) {
-    const int n = weight_row<PHASE>(p, tile, wave * 64 + 16 * s + lr);
-    woff[s] = n < 0 ? kNoRow : (uint32_t)((n * K + 32 * lq) * 2);
-  }
-  // weights of step q = 4 c + j: inputs 128 c + 32 lq + 8 j .. + 8
-  bf16x8 wring[kSharedAhead + 1][kNSub];
-  auto load_w = [&](bf16x8 (&dst)[kNSub], int q) {
-    const int so = uniform(q < nsteps ? ((q >> 2) * kKC + 8 * (q & 3)) * 2 : (int)kNoRow);
-#pragma unroll
-    for (int s = 0; s < kNSub; ++s)
-      dst[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wres, woff[s], so, 0));
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(wbuf + i * 1024), 16, woff[i], so, 0,
+                                               0);
   };
-  const int aread = lr * (kKC * 2);
 
   f32x4 acc[MS][kNSub];
 #pragma unroll
@@ -755,53 +770,50 @@ __device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  copy_a(lds_a0, 0);
-#pragma unroll
-  for (int q = 0; q < kSharedAhead; ++q) load_w(wring[q], q);
-  wait_vm<0>();
-  __builtin_amdgcn_s_barrier();
+  // fragment of step j (inputs 32 j + 8 lq .. + 8 of the stage), row lr of
+  // a 16-row sub-tile
+  const int rbase = lr * kSRow;
+  const int pc0 = 16 * ((0 + lq) ^ sswz(lr));
+  const int pc1 = 16 * ((4 + lq) ^ sswz(lr));
 
-  // One chunk: four steps; the activation copy of chunk c + 1 is issued before
-  // the weight loads of the first step, the weight loads of step q +
-  // kSharedAhead at each step q. Loads complete in issue order, so the wait
-  // before step j leaves in flight the weight loads issued after step q's
-  // (and, for the first steps, the activation copy issued among them).
-  auto chunk = [&](int c, const uint8_t* abuf, uint8_t* anext) {
+  auto stage = [&](int st, const uint8_t* acur, uint8_t* anext) {
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // the stage's copies landed; the other
+                                   // activation buffer's reads are done
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nst) copy_a(anext, st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 a[2][MS], b[2][kNSub];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = 4 * c + j;
-      if (j == 0) copy_a(anext, c + 1);
-      load_w(wring[(j + kSharedAhead) & 3], q + kSharedAhead);
-      if (j < kSharedAhead) wait_vm<4 * kSharedAhead + kAPerWave>();
-      else wait_vm<4 * kSharedAhead>();
-      if (c < nch) {
-        bf16x8 a[MS];
-        const int apc = ((4 * lq + j) ^ aslot(lr)) * 16;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int mi = 0; mi < MS; ++mi)
-          a[mi] = *reinterpret_cast<const bf16x8*>(abuf + mi * 16 * (kKC * 2) + aread + apc);
-#pragma unroll
-        for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-          for (int s = 0; s < kNSub; ++s)
-            acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi], wring[j & 3][s],
-                                                                 acc[mi][s], 0, 0, 0);
-      }
-    }
-    // the activation copy of chunk c + 1 done (the weight loads of the next
-    // kSharedAhead steps may stay in flight); this chunk's LDS reads done
-    wait_vm<4 * kSharedAhead>();
+      for (int s = 0; s < kNSub; ++s)
+        b[j][s] = *reinterpret_cast<const bf16x8*>(wbuf + s * 16 * kSRow + rbase + (j ? pc1 : pc0));
     wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nst) copy_w(st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+        a[j][mi] = *reinterpret_cast<const bf16x8*>(acur + mi * 16 * kSRow + rbase + (j ? pc1 : pc0));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s)
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][mi], b[j][s], acc[mi][s], 0, 0,
+                                                               0);
   };
-  static_assert(kSharedAhead + 1 == 4, "the weight ring has one slot per step of a chunk");
-  // pairs of chunks, so that each buffer is a compile-time choice (the compiler
-  // tells the two apart and does not wait for a copy into one before reading
-  // the other); a padding chunk past an odd count only keeps the loads even
-  for (int c = 0; c < nch; c += 2) {
-    chunk(c, lds_a0, lds_a1);
-    chunk(c + 1, lds_a1, lds_a0);
+  copy_a(lds_a1, 0);
+  copy_w(0);
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, lds_a1, lds_a2);
+    stage(st + 1, lds_a2, lds_a1);
   }
+  wait_lgkm0();
 
   // epilogue: lane holds rows 4 lq + i of each sub-tile, column lr
   if (PHASE == kGateUp) {
@@ -871,8 +883,8 @@ template <int PHASE>
 __device__ __forceinline__ void run_shared(const GemmParams& p, int sid, int n_tiles) {
   const int tb = sid / n_tiles;
   const int tile = sid - tb * n_tiles;
-  const int64_t t0 = (int64_t)tb * kBM;
-  const int64_t rows = p.T - t0 < kBM ? p.T - t0 : kBM;
+  const int64_t t0 = (int64_t)tb * kSBM;
+  const int64_t rows = p.T - t0 < kSBM ? p.T - t0 : kSBM;
   if (rows <= 32) shared_tile<PHASE, 2>(p, t0, tile);
   else if (rows <= 64) shared_tile<PHASE, 4>(p, t0, tile);
   else shared_tile<PHASE, 6>(p, t0, tile);
@@ -942,7 +954,7 @@ hipError_t launch(const GemmParams& p, hipStream_t stream) {
   const int64_t blocks = ((int64_t)p.max_blocks + kXcds - 1) / kXcds * kXcds;
   const int n_tiles = (p.N + tile_cols<PHASE>() - 1) / tile_cols<PHASE>();
   const int nch = p.K / kKC;
-  const int64_t n_shared64 = p.wshared ? (p.T + kBM - 1) / kBM * n_tiles : 0;
+  const int64_t n_shared64 = p.wshared ? (p.T + kSBM - 1) / kSBM * n_tiles : 0;
   // several tiles per work-group only where a tile is a few chunks long
   // (at most 16 chunks per work-group, at most four tiles), over whole tiles
   // and an even chunk count
