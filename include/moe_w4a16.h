@@ -87,7 +87,10 @@ int moe_w4a16_workspace_size(const moe_w4a16_problem *p, size_t *bytes);
 
 /*
  * The bucket granularity (rows per GEMM block) moe_w4a16_forward uses for
- * `p`. Writes *block_m (host). Returns a status.
+ * `p`. Writes *block_m (host). Returns a status. With block_m 96 and fewer
+ * than 8192 (token, slot) pairs, the experts that receive at most 4 pairs are
+ * bucketed in 4 rows instead and computed as in a decode-sized call (see
+ * moe_w4a16_forward); the others use 96-row buckets.
  */
 int moe_w4a16_forward_block_m(const moe_w4a16_problem *p, int32_t *block_m);
 
@@ -155,7 +158,9 @@ int moe_w4a16_align_scratch_size(const moe_w4a16_problem *p, size_t *bytes);
  * products accumulate in fp32. Decode-sized calls (moe_w4a16_forward_block_m
  * 4) put the codes into bf16 MFMAs and multiply each group's fp32 scale
  * after them, with h rounded to bf16. Larger calls (block_m 96) run the
- * routed products in fp16, where (u - 8) * s is exact for bf16 group scales
+ * routed products in fp16 (except experts with at most 4 pairs in a call of
+ * fewer than 8192 pairs, which take the decode-sized path), where (u - 8) * s
+ * is exact for bf16 group scales
  * with 2^-17 <= |s| < 2^13 (smaller ones round to fp16's subnormal grid,
  * larger ones overflow): x is converted once to fp16 with one power-of-two
  * scale per token (exact down to 2^-32 of the token's largest |x|), and h is
@@ -178,7 +183,9 @@ int moe_w4a16_forward(const void *x, const int32_t *topk_ids, const float *topk_
  * GEMM, [3] before the combine, [4] after it, [5] after the gate_up launch and
  * [6] after the down launch (each launch carries the routed and the shared
  * experts; with block_m 96 the conversion of x to fp16 runs between [0] and
- * [1]). Used to time each kernel on its own stream.
+ * [1], and experts in 4-row buckets take a launch of their own just before
+ * each GEMM launch, inside the same interval). Used to time each kernel on
+ * its own stream.
  */
 int moe_w4a16_forward_timed(const void *x, const int32_t *topk_ids, const float *topk_weights,
                             const int32_t *packed_w13, const void *scales_w13,

@@ -108,6 +108,17 @@ hipError_t launch_align(const int32_t*, int64_t P, int32_t E, int32_t, int32_t b
   stub::in_ws(n_padded, 4, "n_padded");
   return hipSuccess;
 }
+hipError_t launch_align_split(const int32_t* ids, int64_t P, int32_t E, int32_t base,
+                              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                              int32_t* n_padded, int32_t tau, int32_t block_m2, int32_t* sorted2,
+                              int32_t* block_expert2, int32_t* n_padded2, hipStream_t s) {
+  if (tau < 0 || block_m2 < 1) ++stub::bad;
+  const int64_t cap2 = P + (P < E ? P : E) * (block_m2 - 1);
+  stub::in_ws(sorted2, 4 * cap2, "sorted_ids (second set)");
+  stub::in_ws(block_expert2, 4 * (cap2 / block_m2), "block_expert (second set)");
+  stub::in_ws(n_padded2, 4, "n_padded (second set)");
+  return launch_align(ids, P, E, base, block_m, sorted_ids, block_expert, n_padded, s);
+}
 hipError_t launch_align_multi(const int32_t* ids, int64_t P, int32_t E, int32_t base,
                               int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                               int32_t* n_padded, int32_t* scratch, hipStream_t s) {

@@ -105,3 +105,48 @@ def test_local_buckets_spanning_blocks(dev):
     ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
                          bank.scales_w2, sw, 0)
     check(mi.bf16_tensor_to_f64(out), ref, "local buckets spanning blocks")
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_split_buckets(dev, shared):
+    """A call with 96-row buckets and fewer than 8192 pairs: experts with at
+    most 4 pairs (here 1, 3 and exactly 4) are bucketed in 4 rows and take the
+    decode-sized kernels, the others (5 pairs, just over, and 40 and more)
+    keep 96-row buckets; an expert without pairs, a non-local id and an
+    invalid id drop out. Both sets in one call, against the oracle, and the
+    prepacked form equal to it bit for bit."""
+    import torch
+
+    import w4a16_int4_grouped_moe_amd as moe
+
+    H, I, E, k, base = 1024, 512, 10, 2, 3  # widths the prepacked layout serves
+    want = [40, 1, 3, 4, 5, 0, 57, 4, 1, 3]  # pairs per local expert
+    valid = np.repeat(np.arange(E, dtype=np.int32), want) + base  # sorted by expert
+    T = (len(valid) + 2) // k
+    s = np.concatenate([valid, np.array([1, -7], np.int32)])  # non-local, invalid
+    # token t takes positions t and t + T of the sorted list: distinct experts,
+    # as no expert holds T or more pairs
+    assert max(want) < T and len(s) == T * k
+    ids = np.stack([s[:T], s[T:]], axis=1)
+    ids = ids[np.random.default_rng(11).permutation(T)]
+    assert moe.forward_block_m(moe.problem(T, H, I, E, k, base)) == 96
+    loc = ids[(ids >= base) & (ids < base + E)] - base
+    assert np.bincount(loc, minlength=E).tolist() == want
+    assert all(ids[t, 0] != ids[t, 1] for t in range(T))
+    w = np.random.default_rng(12).uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    bank = mi.weight_bank(81, H, I, list(range(base, base + E)))
+    bank_dev = {kk: mi.to_device(v, dev) for kk, v in bank.__dict__.items()}
+    x = mi.activations(82, T, H)
+    sw = mi.shared_weights(83, H, I) if shared else None
+    print(f"[case] split buckets T={T} shared={shared}", flush=True)
+    out = run_layer(dev, x, ids, w, bank_dev, sw, base)
+    d = lambda a: mi.to_device(a, dev)
+    pk = moe.prepack(bank_dev["packed_w13"], bank_dev["scales_w13"], bank_dev["packed_w2"],
+                     bank_dev["scales_w2"])
+    out_pk = moe.forward_prepacked(d(x), d(ids), d(w), pk, None if sw is None else d(sw),
+                                   expert_base=base)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_pk.view(torch.int16))
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw, base)
+    check(mi.bf16_tensor_to_f64(out), ref, f"split buckets shared={shared}")

@@ -19,6 +19,11 @@
 //      bit into the expert's 64-bit lane mask in a per-wave LDS table (an OR
 //      does not depend on order), reads the mask back and counts the lower
 //      lanes, so positions are exactly the stable order.
+// Split form (small P only): experts with at most `tau` pairs get their
+// buckets in a second set of arrays with a second block size (bm2); the
+// others keep the first. Each set is the bucketing of its own experts alone
+// (buckets in expert order, padded to its block size), and every valid pair
+// lands in exactly one of them.
 #include "internal.h"
 
 namespace moe {
@@ -96,21 +101,54 @@ __device__ __forceinline__ void pad_buckets(const int32_t* off, const int32_t* c
   }
 }
 
+// Exclusive prefix of v over the work-group's threads (thread order), and the
+// total in *total; wsum: kWaves ints of LDS. Ends with a barrier.
+__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < kWaves ? wsum[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(s, d);
+      if (lane >= d) s += u;
+    }
+    if (lane < kWaves) wsum[lane] = s;
+  }
+  __syncthreads();
+  const int excl = incl - v + (wave > 0 ? wsum[wave - 1] : 0);
+  *total = wsum[kWaves - 1];
+  __syncthreads();
+  return excl;
+}
+
 __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int64_t P, int E, int base, int bm,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ n_padded_out) {
+    int32_t* __restrict__ n_padded_out, int tau, int bm2, int32_t* __restrict__ sorted2,
+    int32_t* __restrict__ block_expert2, int32_t* __restrict__ n_padded2_out) {
   extern __shared__ int32_t smem[];
   int32_t* hist = smem;                      // [kWaves][E]: counts, then write cursors
-  int32_t* off = smem + kWaves * E;          // [E] bucket start
-  int32_t* cnt = off + E;                    // [E] valid pairs per expert
+  int32_t* off = smem + kWaves * E;          // [E] bucket start (first set)
+  int32_t* cnt = off + E;                    // [E] valid pairs per expert (first set)
   int32_t* wsum = cnt + E;                   // [kWaves] scan partials
   // [kWaves][E] lane masks; the offset, 4 (18 E + 16) bytes, is a multiple of 8
   uint64_t* masks = reinterpret_cast<uint64_t*>(smem + kWaves * E + 2 * E + kWaves);
+  // split form: [E] bucket start and pairs in the second set
+  int32_t* off2 = reinterpret_cast<int32_t*>(masks + kWaves * E);
+  int32_t* cnt2 = off2 + E;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool split = tau >= 0;
 
   for (int i = tid; i < kWaves * E; i += kThreads) {
     hist[i] = 0;
@@ -130,45 +168,48 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   }
   __syncthreads();
 
-  // 2. totals, per-wave prefixes and the bucket offsets
-  int pad = 0;
+  // 2. totals, per-wave prefixes and the bucket offsets (per set)
+  int run = 0;
+  bool first = true;  // the expert's buckets are in the first set
   if (tid < E) {
-    int run = 0;
     for (int w = 0; w < kWaves; ++w) {
       const int c = hist[w * E + tid];
       hist[w * E + tid] = run;
       run += c;
     }
-    cnt[tid] = run;
-    pad = (run + bm - 1) / bm * bm;
+    first = !split || run > tau;
   }
-  int incl = pad;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(incl, d);
-    if (lane >= d) incl += u;
+  const int pad = tid < E && first ? (run + bm - 1) / bm * bm : 0;
+  int total;
+  const int excl = block_exclusive_scan(pad, wsum, &total);
+  if (tid < E) {
+    off[tid] = excl;
+    cnt[tid] = first ? run : 0;
   }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    int s = lane < kWaves ? wsum[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int u = __shfl_up(s, d);
-      if (lane >= d) s += u;
+  if (tid == 0) *n_padded_out = total;
+  int excl2 = 0;
+  if (split) {
+    const int pad2 = tid < E && !first ? (run + bm2 - 1) / bm2 * bm2 : 0;
+    int total2;
+    excl2 = block_exclusive_scan(pad2, wsum, &total2);
+    if (tid < E) {
+      off2[tid] = excl2;
+      cnt2[tid] = first ? 0 : run;
     }
-    if (lane < kWaves) wsum[lane] = s;
+    if (tid == 0) *n_padded2_out = total2;
   }
   __syncthreads();
-  const int excl = incl - pad + (wave > 0 ? wsum[wave - 1] : 0);
-  if (tid < E) off[tid] = excl;
-  if (tid == kThreads - 1) *n_padded_out = excl + pad;
-  __syncthreads();
-  for (int i = tid; i < kWaves * E; i += kThreads) hist[i] += off[i % E];
+  // write cursors: bucket start + the pairs of earlier waves; the set is
+  // told apart by the cursor's sign bit (second set: ~cursor)
+  for (int i = tid; i < kWaves * E; i += kThreads) {
+    const int e = i % E;
+    hist[i] = (!split || cnt2[e] == 0) ? off[e] + hist[i] : ~(off2[e] + hist[i]);
+  }
   __syncthreads();
 
   // 3. sentinel padding and the block map (positions the scatter never writes)
   pad_buckets(off, cnt, E, bm, (int32_t)P, tid, kWaves, sorted_ids, block_expert);
+  if (split) pad_buckets(off2, cnt2, E, bm2, (int32_t)P, tid, kWaves, sorted2, block_expert2);
 
   // 4. stable scatter, 64 pairs at a time in pair order
   uint64_t* const wmask = masks + wave * E;
@@ -185,9 +226,10 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     const int group = __popcll(m);
     if (e >= 0) {
       const int cursor = hist[wave * E + e];
-      sorted_ids[cursor + rank] = (int32_t)p;
+      if (cursor >= 0) sorted_ids[cursor + rank] = (int32_t)p;
+      else sorted2[~cursor + rank] = (int32_t)p;
       if (rank == 0) {
-        hist[wave * E + e] = cursor + group;
+        hist[wave * E + e] = cursor >= 0 ? cursor + group : cursor - group;
         clear_lane_group(wmask, e);
       }
     }
@@ -348,14 +390,25 @@ hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int
   return hipGetLastError();
 }
 
+hipError_t launch_align_split(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
+                              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                              int32_t* n_padded, int32_t tau, int32_t block_m2,
+                              int32_t* sorted2, int32_t* block_expert2, int32_t* n_padded2,
+                              hipStream_t stream) {
+  if (E > kMaxExperts || P > 0x3fffffff) return hipErrorInvalidValue;
+  const size_t lds = sizeof(int32_t) * (size_t)(kWaves * E + 2 * E + kWaves) +
+                     sizeof(uint64_t) * kWaves * E + (tau >= 0 ? sizeof(int32_t) * 2 * E : 0);
+  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), lds, stream, topk_ids, P, E, base,
+                     block_m, sorted_ids, block_expert, n_padded, tau, block_m2, sorted2,
+                     block_expert2, n_padded2);
+  return hipGetLastError();
+}
+
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* n_padded, hipStream_t stream) {
-  const size_t lds =
-      sizeof(int32_t) * (size_t)(kWaves * E + 2 * E + kWaves) + sizeof(uint64_t) * kWaves * E;
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kThreads), lds, stream, topk_ids, P, E, base,
-                     block_m, sorted_ids, block_expert, n_padded);
-  return hipGetLastError();
+  return launch_align_split(topk_ids, P, E, base, block_m, sorted_ids, block_expert, n_padded, -1,
+                            1, nullptr, nullptr, nullptr, stream);
 }
 
 }  // namespace moe

@@ -15,6 +15,14 @@ constexpr int kMaxExperts = 512;
 hipError_t launch_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                         int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* n_padded, hipStream_t stream);
+// The split form (one work-group): experts with at most tau pairs are
+// bucketed into the second set of arrays with block size block_m2, the others
+// into the first; each set as launch_align would bucket its experts alone.
+hipError_t launch_align_split(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
+                              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                              int32_t* n_padded, int32_t tau, int32_t block_m2,
+                              int32_t* sorted2, int32_t* block_expert2, int32_t* n_padded2,
+                              hipStream_t stream);
 int64_t align_scratch_ints(int64_t P, int32_t E);
 hipError_t launch_align_multi(const int32_t* topk_ids, int64_t P, int32_t E, int32_t base,
                               int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
