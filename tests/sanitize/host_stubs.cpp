@@ -113,7 +113,12 @@ hipError_t launch_align_split(const int32_t* ids, int64_t P, int32_t E, int32_t 
                               int32_t* n_padded, int32_t tau, int32_t block_m2, int32_t* sorted2,
                               int32_t* block_expert2, int32_t* n_padded2, hipStream_t s) {
   if (tau < 0 || block_m2 < 1) ++stub::bad;
-  const int64_t cap2 = P + (P < E ? P : E) * (block_m2 - 1);
+  // the second set holds experts of at most tau pairs: ceil(tau / block_m2)
+  // blocks each at most
+  const int64_t emin = P < E ? P : E;
+  const int64_t full = P + emin * (block_m2 - 1);
+  const int64_t tight = block_m2 * ((tau + block_m2 - 1) / block_m2) * emin;
+  const int64_t cap2 = full < tight ? full : tight;
   stub::in_ws(sorted2, 4 * cap2, "sorted_ids (second set)");
   stub::in_ws(block_expert2, 4 * (cap2 / block_m2), "block_expert (second set)");
   stub::in_ws(n_padded2, 4, "n_padded (second set)");

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/moe_w4a16.h"
@@ -132,7 +133,12 @@ Layout layout(const moe_w4a16_problem* p) {
   L.split = split_buckets(p, L.bm);
   L.sorted2 = L.block2 = L.meta2 = L.h2 = o;
   if (L.split) {
-    L.cap_rows2 = sorted_capacity(p, 4);
+    // an expert of the 4-row set holds at most kSplitMaxPairs pairs: at most
+    // ceil(kSplitMaxPairs / 4) blocks each (the launches over this set size
+    // their grids by it, and its blocks past the count exit at once)
+    const int64_t P64 = (int64_t)P, E64 = p->num_experts;
+    const int64_t per = (kSplitMaxPairs + 3) / 4;
+    L.cap_rows2 = std::min<int64_t>(sorted_capacity(p, 4), 4 * per * std::min(E64, P64));
     L.max_blocks2 = (int32_t)(L.cap_rows2 / 4);
     L.sorted2 = o; o = round_up(o + 4 * (size_t)L.cap_rows2);
     L.block2 = o; o = round_up(o + 4 * (size_t)L.max_blocks2);
