@@ -109,12 +109,19 @@ class Hip:
         return ms.value
 
 
-def traffic_record(name, bm):
-    """rocprofv3 FETCH_SIZE / WRITE_SIZE of the gate_up kernel (record `name`,
-    e.g. "decode" or "prefill_prepacked"), if the record in profiles/ was
-    taken on the current source of that kernel."""
-    src = os.path.join(CSRC, KERNEL_SRC[bm])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+def sources_sha(files):
+    """sha256 over the concatenated bytes of kernel sources (csrc/ names)."""
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_record(name, srcs):
+    """rocprofv3 FETCH_SIZE / WRITE_SIZE of the gate_up launch or launches
+    (record `name`, e.g. "decode" or "prefill_prepacked"), if the record in
+    profiles/ was taken on the current sources `srcs` of those kernels."""
+    sha = sources_sha(srcs)
     path = os.path.join(ROOT, "profiles", f"gate_up_{name}_traffic.md")
     if not os.path.exists(path):
         return None, path
@@ -122,7 +129,8 @@ def traffic_record(name, bm):
         m = re.match(r"\s*traffic_record:\s*(\{.*\})\s*$", line)
         if m:
             rec = json.loads(m.group(1))
-            if rec.get("kernel_source_sha256") == sha:
+            if (rec.get("kernel_sources", [srcs[0]]) == list(srcs)
+                    and rec.get("kernel_source_sha256") == sha):
                 return rec, path
     return None, path
 
@@ -198,7 +206,8 @@ class Leg:
                 out=torch.empty((T, g.hidden), dtype=torch.bfloat16, device=dev),
                 ws=torch.empty(max(moe.workspace_size(p), 1), dtype=torch.uint8, device=dev),
                 work=work(T, g.hidden, g.inter, g.top_k, ids, w.n_local, w.expert_base, g.shared),
-                bm=moe.forward_block_m(p), base=w.expert_base)
+                bm=moe.forward_block_m(p), split=moe.forward_split_max_pairs(p),
+                base=w.expert_base)
             if prepacked:  # the weight copy is replaced by its prepacked form
                 c["pk"] = moe.prepack(*c["args"][3:7])
                 c["args"] = c["args"][:3] + (None, None, None, None) + c["args"][7:]
@@ -284,7 +293,12 @@ def roofline(leg, gu_ms, bound):
 
     mean_s = float(np.mean([np.mean(g) for g in gu_ms])) / 1e3
     bm = leg.calls[0]["bm"]
-    rec, path = traffic_record(leg.record_name(), bm)
+    # the split bucketing adds a small-batch launch over the experts with a
+    # few pairs before the 96-row launch: the roofline is then the gate_up
+    # phase (both launches; the events bracket them together)
+    split = bm == 96 and any(c["split"] for c in leg.calls)
+    srcs = [KERNEL_SRC[4], KERNEL_SRC[96]] if split else [KERNEL_SRC[bm]]
+    rec, path = traffic_record(leg.record_name(), srcs)
     if bound == "mfma":
         alg = float(np.mean([c["work"]["gate_up_flops"] for c in leg.calls]))
         ach = alg / mean_s / 1e12
@@ -298,9 +312,12 @@ def roofline(leg, gu_ms, bound):
     r["traffic"] = (rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]) if rec else None
     r["traffic_source"] = (
         f"recorded: rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel and workload in "
-        f"{os.path.relpath(path, ROOT)}, taken on the current {KERNEL_SRC[bm]}" if rec else
-        f"no rocprofv3 record for the current {KERNEL_SRC[bm]} ({os.path.relpath(path, ROOT)})")
-    r["kernel"] = KERNEL_NAME[bm]
+        f"{os.path.relpath(path, ROOT)}, taken on the current {' + '.join(srcs)}" if rec else
+        f"no rocprofv3 record for the current {' + '.join(srcs)} ({os.path.relpath(path, ROOT)})")
+    r["kernel"] = (
+        "gate_up phase, two launches: small_gemm_kernel<gate_up> over the 4-row buckets of the "
+        f"experts with at most {max(c['split'] for c in leg.calls)} pairs, then "
+        + KERNEL_NAME[96] if split else KERNEL_NAME[bm])
     r["algorithmic_per_launch"] = alg
     r["avg_launch_us"] = round(mean_s * 1e6, 2)
     return r

@@ -95,6 +95,14 @@ int moe_w4a16_workspace_size(const moe_w4a16_problem *p, size_t *bytes);
 int moe_w4a16_forward_block_m(const moe_w4a16_problem *p, int32_t *block_m);
 
 /*
+ * The split of the bucketing moe_w4a16_forward uses for `p`: writes to
+ * *max_pairs (host) the largest pair count of an expert that is bucketed in
+ * 4 rows beside the 96-row buckets (4 at present), or 0 when the call has no
+ * such split (block_m 4, or 8192 pairs or more). Returns a status.
+ */
+int moe_w4a16_forward_split_max_pairs(const moe_w4a16_problem *p, int32_t *max_pairs);
+
+/*
  * Capacities moe_w4a16_align needs: *sorted_capacity int32 entries for
  * sorted_ids and *block_capacity entries for block_expert (both host out).
  * sorted_capacity = T*k + min(E, T*k) * (block_m - 1), the largest possible

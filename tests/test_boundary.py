@@ -33,6 +33,7 @@ def test_header_declares_expected_entry_points():
         "moe_w4a16_align", "moe_w4a16_align_capacity", "moe_w4a16_align_scratch_size",
         "moe_w4a16_forward",
         "moe_w4a16_forward_block_m", "moe_w4a16_forward_scores", "moe_w4a16_forward_timed",
+        "moe_w4a16_forward_split_max_pairs",
         "moe_w4a16_forward_noalloc", "moe_w4a16_noalloc_workspace_limit",
         "moe_w4a16_forward_prepacked", "moe_w4a16_forward_prepacked_timed",
         "moe_w4a16_prepack", "moe_w4a16_prepack_size",
@@ -73,6 +74,13 @@ def test_workspace_size_and_block_m(lib):
     assert moe.forward_block_m(P(num_tokens=193)) == 96
     assert moe.forward_block_m(P(num_tokens=512)) == 96
     assert moe.forward_block_m(P(num_tokens=4096)) == 96
+    # the split bucketing: 96-row calls of fewer than 8192 pairs put experts
+    # with at most 4 pairs in 4-row buckets
+    assert moe.forward_split_max_pairs(P()) == 0                    # block_m 4
+    assert moe.forward_split_max_pairs(P(num_tokens=193)) == 4
+    assert moe.forward_split_max_pairs(P(num_tokens=1023)) == 4     # 8184 pairs
+    assert moe.forward_split_max_pairs(P(num_tokens=1024)) == 0     # 8192 pairs
+    assert moe.forward_split_max_pairs(P(num_tokens=4096)) == 0
     # widths that are not whole block tiles (7040 % 512 != 0, 1152 % 256 != 0)
     # take the same 96-row blocks, masked
     assert moe.forward_block_m(P(num_tokens=512, hidden=7040)) == 96

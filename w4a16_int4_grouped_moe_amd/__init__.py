@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     align_scratch_size,
     forward,
     forward_block_m,
+    forward_split_max_pairs,
     forward_noalloc,
     forward_prepacked,
     forward_scores,

@@ -55,6 +55,7 @@ def library():
         PP = ctypes.POINTER(Problem)
         lib.moe_w4a16_workspace_size.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_w4a16_forward_block_m.argtypes = [PP, ctypes.POINTER(ctypes.c_int32)]
+        lib.moe_w4a16_forward_split_max_pairs.argtypes = [PP, ctypes.POINTER(ctypes.c_int32)]
         lib.moe_w4a16_align_capacity.argtypes = [PP, ctypes.c_int32,
                                                  ctypes.POINTER(ctypes.c_int64),
                                                  ctypes.POINTER(ctypes.c_int64)]
@@ -111,6 +112,14 @@ def workspace_size(p: Problem) -> int:
 def forward_block_m(p: Problem) -> int:
     v = ctypes.c_int32(0)
     _check(library().moe_w4a16_forward_block_m(ctypes.byref(p), ctypes.byref(v)))
+    return v.value
+
+
+def forward_split_max_pairs(p: Problem) -> int:
+    """Experts with at most this many pairs take 4-row buckets beside the
+    96-row ones in this call (0: no split)."""
+    v = ctypes.c_int32(0)
+    _check(library().moe_w4a16_forward_split_max_pairs(ctypes.byref(p), ctypes.byref(v)))
     return v.value
 
 

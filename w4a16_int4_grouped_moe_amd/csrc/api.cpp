@@ -176,6 +176,14 @@ int moe_w4a16_forward_block_m(const moe_w4a16_problem* p, int32_t* block_m) {
   return MOE_OK;
 }
 
+int moe_w4a16_forward_split_max_pairs(const moe_w4a16_problem* p, int32_t* max_pairs) {
+  const int st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!max_pairs) return MOE_ERR_NULL;
+  *max_pairs = split_buckets(p, choose_block_m(p)) ? kSplitMaxPairs : 0;
+  return MOE_OK;
+}
+
 int moe_w4a16_align_capacity(const moe_w4a16_problem* p, int32_t block_m,
                              int64_t* sorted_cap, int64_t* block_cap) {
   const int st = check_problem(p);
