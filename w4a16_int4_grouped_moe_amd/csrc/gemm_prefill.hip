@@ -116,6 +116,12 @@ constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, dword 3
 static_assert(kBN == kPackRows && kKC == kPackChunk, "tiles of the prepacked layout");
 static_assert(kHTile == kBN / 2, "h exponent tiles are the gate_up column tiles");
 constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
+#ifndef MOE_PREFILL_ODD_SUBTILES
+#define MOE_PREFILL_ODD_SUBTILES 1
+#endif
+// blocks of 33-48 and 65-80 rows run the K loop for 3 and 5 sub-tiles
+// (otherwise 4 and 6)
+constexpr bool kOddSubtiles = MOE_PREFILL_ODD_SUBTILES != 0;
 constexpr int kSBM = kBM;                  // tokens per shared-expert work-group
 constexpr int kSKC = 64;                   // inputs per shared-expert stage
 constexpr int kSRow = kSKC * 2;            // bytes of a row per stage: one 128-byte line
@@ -870,6 +876,11 @@ __device__ __forceinline__ void run_block(const GemmParams& p, int mblk, int til
     n_valid += __popcll(__ballot(r < kBM && p.sorted_ids[row0 + r] < p.P));
   }
   const int msub = uniform((n_valid + 15) >> 4);
+  if (kOddSubtiles && kMaxMS == 6 && (msub == 3 || msub == 5)) {
+    if (msub == 3) block_tile<PHASE, 3, PK, MT>(p, mblk, tile, ntl);
+    else block_tile<PHASE, 5, PK, MT>(p, mblk, tile, ntl);
+    return;
+  }
   if (msub <= 2) block_tile<PHASE, 2, PK, MT>(p, mblk, tile, ntl);
   else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4), PK, MT>(p, mblk, tile, ntl);
   else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6), PK, MT>(p, mblk, tile, ntl);
