@@ -22,6 +22,12 @@ expert), timed in two legs:
     (routed experts and the shared expert: algorithmic FLOPs per launch over
     its average duration).
 
+Secondary outputs: p10/p90 of the per-call times next to the median, warm
+back-to-back calls on one weight copy and replays of a call captured in a HIP
+graph (`per_batch`), and `achievable`: what this GPU reaches on a 1 GiB
+device copy and a bf16 library GEMM (measurement denominators only), with
+each roofline's `frac_of_achievable`.
+
 Inputs are seeded synthetic data, resident in HBM before timing starts. Launch
 durations come from HIP events that the library records around the launch on
 its own stream during the timed steps. `traffic` is the HBM traffic that
@@ -263,6 +269,36 @@ class Leg:
         return [[hip.elapsed_ms(ev[s][ci][0], ev[s][ci][4]) for s in range(n)]
                 for ci in range(len(self.calls))]
 
+    def warm_and_graph(self, n):
+        """Secondary timings per batch: n back-to-back calls on the same
+        weights (warm caches), and n replays of one call captured in a HIP
+        graph (no host launch cost). Returns [(warm_ms, graph_ms)] per call."""
+        import torch
+
+        out = []
+        for c in self.calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            self.run(c)
+            a.record()
+            for _ in range(n):
+                self.run(c)
+            b.record()
+            torch.cuda.synchronize()
+            warm = a.elapsed_time(b) / n
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.run(c)
+            g.replay()
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(n):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out.append((warm, a.elapsed_time(b) / n))
+            del g
+        return out
+
     def diag(self, hip, n):
         """n more steps with all stage events (after the timed region): stage
         durations (ms) per call, shape [call][step][stage], and the routed
@@ -323,7 +359,7 @@ def roofline(leg, gu_ms, bound):
     return r
 
 
-def per_batch(leg, call_ms, st, gu_diag, dn_diag, gu_timed, route_us=None):
+def per_batch(leg, call_ms, st, gu_diag, dn_diag, gu_timed, route_us=None, warm_graph=None):
     import numpy as np
 
     out = []
@@ -333,6 +369,8 @@ def per_batch(leg, call_ms, st, gu_diag, dn_diag, gu_timed, route_us=None):
         wk = c["work"]
         d = dict(
             T=c["T"], us_per_call=round(call_s * 1e6, 2),
+            us_per_call_p10_p90=[round(float(np.percentile(call_ms[ci], q)) * 1e3, 2)
+                                 for q in (10, 90)],
             tokens_per_s=round(c["T"] / call_s, 1),
             layer_hbm_gbs=round(wk["layer_bytes"] / call_s / 1e9, 1),
             layer_hbm_frac=round(wk["layer_bytes"] / call_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -345,8 +383,60 @@ def per_batch(leg, call_ms, st, gu_diag, dn_diag, gu_timed, route_us=None):
             stage_us_with_events={n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, s.mean(0))})
         if route_us is not None:
             d["router_us"] = round(route_us[ci], 2)
+        if warm_graph is not None:
+            d["warm_back_to_back_us"] = round(warm_graph[ci][0] * 1e3, 2)
+            d["graph_replay_us"] = round(warm_graph[ci][1] * 1e3, 2)
         out.append(d)
     return out
+
+
+def achievable(dev):
+    """Secondary denominators measured on this GPU: a 1 GiB device copy (read +
+    write), a 1 GiB sum (read), and a bf16 8192^3 library GEMM (measurement
+    only; no part of the layer uses it)."""
+    import torch
+
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        dst.copy_(src)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 10 / (a.elapsed_time(b) / 1e3) / 1e9
+    del dst
+    for _ in range(3):
+        t = src.sum()
+    a.record()
+    for _ in range(10):
+        t = src.sum()
+    b.record()
+    torch.cuda.synchronize()
+    read_gbs = (1 << 30) * 10 / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, t
+    gbs = max(copy_gbs, read_gbs)
+    n = 8192
+    x = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    y = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    for _ in range(3):
+        z = torch.matmul(x, y)
+    a.record()
+    for _ in range(10):
+        z = torch.matmul(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    tfs = 2 * n ** 3 * 10 / (a.elapsed_time(b) / 1e3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"hbm_gbs": round(gbs, 1), "copy_gbs": round(copy_gbs, 1),
+            "read_gbs": round(read_gbs, 1), "bf16_tflops": round(tfs, 1),
+            "method": "HBM: the better of a 1 GiB device copy (bytes read + written) and a "
+                      "1 GiB sum (bytes read); MFMA: bf16 8192x8192x8192 matmul (library "
+                      "GEMM, measurement only)"}
 
 
 def router_times(leg, dev, n):
@@ -436,9 +526,10 @@ def main():
     ms_per_step, gu = leg.time(hip, args.steps, args.warmup)
     value = sum(batches) / (ms_per_step / 1e3)
     n_diag = min(5, args.steps)
-    call_ms = leg.call_times(hip, max(n_diag, 10))
+    call_ms = leg.call_times(hip, 20)
     st, gu_d, dn_d = leg.diag(hip, n_diag)
     route_us = router_times(leg, dev, n_diag)
+    warm_graph = leg.warm_and_graph(10)
     roof = roofline(leg, gu, "hbm" if hbm_bound else "mfma")
     print(f"[bench] {args.workload}: {ms_per_step:.4f} ms/step, {value:.1f} tokens/s",
           file=sys.stderr, flush=True)
@@ -477,8 +568,9 @@ def main():
         print(f"[bench] prefill setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr,
               flush=True)
         ms_p, gu_p = pleg.time(hip, args.steps, args.warmup)
-        call_p = pleg.call_times(hip, n_diag)
+        call_p = pleg.call_times(hip, 10)
         st_p, gu_pd, dn_pd = pleg.diag(hip, n_diag)
+        warm_graph_p = pleg.warm_and_graph(5)
         wk = pleg.calls[0]["work"]
         prefill = {
             "workload": describe("prefill", [4096], pleg.g), "T": 4096,
@@ -489,7 +581,8 @@ def main():
             "dtype": "routed products fp16 x fp16 (exact dequantised weights), shared expert "
                      "bf16 x bf16, fp32 accumulation",
             "roofline": roofline(pleg, gu_p, "mfma"),
-            "per_batch": per_batch(pleg, call_p, st_p, gu_pd, dn_pd, gu_p),
+            "per_batch": per_batch(pleg, call_p, st_p, gu_pd, dn_pd, gu_p,
+                                   warm_graph=warm_graph_p),
         }
         print(f"[bench] prefill: {ms_p:.4f} ms/layer", file=sys.stderr, flush=True)
         if args.cpu_tokens > 0:
@@ -501,6 +594,12 @@ def main():
     if args.cpu_tokens > 0:
         cpu = cpu_baseline(leg.calls, leg.shared_np, args.cpu_tokens, args.cpu_seconds)
 
+    # secondary denominators: what this GPU reaches on plain copies and GEMMs
+    ach = achievable(dev)
+    for r in [roof] + ([prefill["roofline"]] if prefill else []):
+        den = ach["hbm_gbs"] if r["bound"] == "hbm" else ach["bf16_tflops"]
+        r["frac_of_achievable"] = round(r["achieved"] / den, 4)
+
     g = leg.g
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -508,14 +607,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if leg.calls[0]["bm"] == 4 else "fp16 (routed) / bf16 (shared)",
         "data": "synthetic (seeded: int4 codes uniform, bf16 scales U(0.005,0.02), "
-                "x N(0,1), uniform distinct top-k routing, softmax weights)",
+                "x N(0,1), " + ("Zipf(1.2) top-k routing" if leg.w0.routing == "zipf" else
+                                "uniform distinct top-k routing") + ", softmax weights)",
         "config": {"workload": describe(args.workload, batches, g), "batches": batches,
                    "hidden": g.hidden, "inter": g.inter,
                    "weights": "prepacked" if args.prepacked else "checkpoint layout",
                    "experts": leg.w0.n_local, "top_k": g.top_k, "shared_expert": g.shared,
                    "block_m": [c["bm"] for c in leg.calls]},
-        "per_batch": per_batch(leg, call_ms, st, gu_d, dn_d, gu, route_us),
+        "per_batch": per_batch(leg, call_ms, st, gu_d, dn_d, gu, route_us, warm_graph),
         "roofline": roof,
+        "achievable": ach,
         "cpu_baseline": cpu,
         "prefill": prefill,
         "prepacked": prepacked,

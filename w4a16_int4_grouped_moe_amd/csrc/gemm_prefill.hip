@@ -84,6 +84,10 @@ constexpr int kPrefillAux = MOE_PREFILL_AUX;
 #define MOE_PREFILL_SCHED 1
 #endif
 constexpr int kPrefillSched = MOE_PREFILL_SCHED;
+#ifndef MOE_PREFILL_PRIO
+#define MOE_PREFILL_PRIO 0
+#endif
+constexpr int kPrefillPrio = MOE_PREFILL_PRIO;  // wave priority around a sub-tile's MFMAs
 constexpr int kPrefillPackedAux = 2;
 
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
@@ -518,9 +522,11 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 #pragma unroll
       for (int s = 0; s < kNSub; ++s) {
         const h16x8 b = dequant8(w[s][j], sc[s]);
+        if (kPrefillPrio) __builtin_amdgcn_s_setprio(kPrefillPrio);
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi)
           acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], b, acc[mi][s], 0, 0, 0);
+        if (kPrefillPrio) __builtin_amdgcn_s_setprio(0);
       }
       if (kPrefillSched == 1) {
         __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
