@@ -126,7 +126,11 @@ constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
 // blocks of 33-48 and 65-80 rows run the K loop for 3 and 5 sub-tiles
 // (otherwise 4 and 6)
 constexpr bool kOddSubtiles = MOE_PREFILL_ODD_SUBTILES != 0;
-constexpr int kSBM = kBM;                  // tokens per shared-expert work-group
+#ifndef MOE_SHARED_TOKENS
+#define MOE_SHARED_TOKENS 128
+#endif
+constexpr int kSBM = MOE_SHARED_TOKENS;    // tokens per shared-expert work-group
+static_assert(kSBM % 32 == 0 && kSBM <= 128, "shared token block: 2..8 sub-tiles");
 constexpr int kSKC = 64;                   // inputs per shared-expert stage
 constexpr int kSRow = kSKC * 2;            // bytes of a row per stage: one 128-byte line
 
@@ -904,7 +908,8 @@ __device__ __forceinline__ void run_shared(const GemmParams& p, int sid, int n_t
   const int64_t rows = p.T - t0 < kSBM ? p.T - t0 : kSBM;
   if (rows <= 32) shared_tile<PHASE, 2>(p, t0, tile);
   else if (rows <= 64) shared_tile<PHASE, 4>(p, t0, tile);
-  else shared_tile<PHASE, 6>(p, t0, tile);
+  else if (rows <= 96 || kSBM <= 96) shared_tile<PHASE, 6>(p, t0, tile);
+  else shared_tile<PHASE, kSBM / 16>(p, t0, tile);
 }
 
 // Shared-expert work-groups first (ids below n_shared), then one per
