@@ -126,6 +126,36 @@ constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
 // blocks of 33-48 and 65-80 rows run the K loop for 3 and 5 sub-tiles
 // (otherwise 4 and 6)
 constexpr bool kOddSubtiles = MOE_PREFILL_ODD_SUBTILES != 0;
+#ifndef MOE_PREFILL_WLDS
+#define MOE_PREFILL_WLDS 1
+#endif
+// checkpoint-layout blocks of one tile per work-group stage their weights
+// through LDS in whole lines (block_tile_w); otherwise straight into
+// registers (block_tile)
+constexpr bool kWeightsLds = MOE_PREFILL_WLDS != 0;
+#ifndef MOE_PREFILL_WLDS_AUX
+#define MOE_PREFILL_WLDS_AUX 2
+#endif
+// cache policy of those whole-line weight copies: non-temporal (each line is
+// used once, by one copy; kept out of the way of the activation chunks that
+// the block's other column tiles read from L2)
+constexpr int kWLdsAux = MOE_PREFILL_WLDS_AUX;
+#ifndef MOE_PREFILL_STEP_PRIO
+#define MOE_PREFILL_STEP_PRIO 1
+#endif
+constexpr bool kStepPrio = MOE_PREFILL_STEP_PRIO != 0;
+#ifndef MOE_PREFILL_WLDS_SCHED
+#define MOE_PREFILL_WLDS_SCHED 0
+#endif
+// instruction order of an MFMA step in that tile (as kPrefillSched); the
+// compiler's own order measured 2-3% faster there than the fixed interleave
+constexpr int kWLdsSched = MOE_PREFILL_WLDS_SCHED;
+#ifndef MOE_PREFILL_APIPE
+#define MOE_PREFILL_APIPE 0
+#endif
+// LDS-staged tile: the activation fragments of an MFMA step are read during
+// the previous step (two register sets)
+constexpr bool kAPipe = MOE_PREFILL_APIPE != 0;
 #ifndef MOE_SHARED_TOKENS
 #define MOE_SHARED_TOKENS 128
 #endif
@@ -159,6 +189,8 @@ __shared__ __attribute__((aligned(1024))) uint8_t lds_sc[kWaves][kScBuf];
 // down: the row's largest h tile exponent), the h tile exponent being chosen,
 // and the per-wave maxima it is chosen from
 __shared__ int32_t lds_rexp[kBM];
+// down, staged epilogue: the pair id of each block row (the y row it writes)
+__shared__ int32_t lds_rpair[kBM];
 __shared__ int32_t lds_rkh[kBM];
 __shared__ float lds_rmax[kWaves][kBM];
 
@@ -253,6 +285,11 @@ constexpr int tile_cols() { return PHASE == kGateUp ? kBN / 2 : kBN; }
 // sixteen pieces of activation row r.
 __device__ __forceinline__ int wslot(int R) { return (R >> 1) & 3; }
 __device__ __forceinline__ int aslot(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Permutation of the 16-byte pieces of a 128-byte row staged in LDS (the
+// shared-expert operands, the routed weights of the LDS-staged tile): piece
+// P of row r sits in slot P ^ sswz(r), so that 16 rows read at one piece
+// fall in distinct banks.
+__device__ __forceinline__ int sswz(int r) { return (r >> 1) & 7; }
 
 // Output column (h column for gate_up, y column for down) of work-group row
 // R = 64 wave + 16 sub-tile + r; gate_up sub-tiles 0, 1 are gate rows, 2, 3
@@ -346,6 +383,207 @@ __global__ __launch_bounds__(kConvThreads) void h_rescale_kernel(uint16_t* __res
   }
 }
 
+// ---- routed blocks: activation copies and row exponents -------------------------
+// A block's activations reach LDS in chunks of kBM rows x 128 inputs (256
+// bytes per row); copy instruction u covers LDS rows 4u..4u+3 (16 lanes per
+// row, 16 bytes each: whole lines), kAPW instructions per wave and chunk.
+constexpr int kAPW = kBM / 4 / kWaves;
+static_assert((kBM / 4) % kWaves == 0, "activation copies per wave");
+
+template <int PHASE>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_act_rsrc(const GemmParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_routed, 0,
+      (int)((PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM) * p.K * 2), kBufferFlags);
+}
+
+// Source offsets of this lane's activation copies: row 4 (kAPW wave + i) +
+// lane / 16, piece lane % 16 stored at the permuted slot; rows past the
+// block's sub-tiles and padding rows read zeros.
+template <int PHASE, int MS>
+__device__ __forceinline__ void block_act_offsets(const GemmParams& p, int64_t row0,
+                                                  uint32_t (&aoff)[kAPW]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < kAPW; ++i) {
+    const int row = 4 * (kAPW * wave + i) + (lane >> 4);
+    const int piece = (lane & 15) ^ aslot(row & 15);
+    int64_t src = -1;
+    if (row < MS * 16) {
+      if (PHASE == kGateUp) {
+        const int32_t pair = p.sorted_ids[row0 + row];
+        if (pair < p.P) src = pair / p.k;
+      } else {
+        src = row0 + row;
+      }
+    }
+    aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * p.K + piece * 8) * 2);
+  }
+}
+
+// Per-row activation exponents for the epilogue (gate_up: the token's; down:
+// the row's, after h_rescale_kernel), into lds_rexp.
+template <int PHASE, int MS, bool STAGE = false>
+__device__ __forceinline__ void block_row_exps(const GemmParams& p, int64_t row0) {
+  const int tid = threadIdx.x;
+  if (tid < kBM) {
+    int v = 0;
+    if (PHASE == kGateUp) {
+      const int32_t pair = p.sorted_ids[row0 + tid];
+      if (pair < p.P) v = p.a_exp[pair / p.k];
+    } else if (tid < MS * 16) {
+      v = p.a_exp[row0 + tid];
+    }
+    lds_rexp[tid] = v;
+    if (PHASE == kDown && STAGE) lds_rpair[tid] = tid < MS * 16 ? p.sorted_ids[row0 + tid] : INT32_MAX;
+  }
+}
+
+// Epilogue of a routed block tile: lane holds rows 4 lq + i of each 16-row
+// sub-tile, column lr. STAGE: the wave's 8 KB of lds_a0 is free (every copy
+// into LDS has landed and every wave is past its last fragment read), and the
+// outputs go through it so that each lane stores 16 bytes of a row at a time:
+// one store instruction per 16 rows x 16 columns of fp32 (or 32 of fp16)
+// instead of one per 4 rows x 16 columns. (A vector-memory instruction costs
+// its 64 addresses whatever their width; the 2- and 4-byte stores of the
+// plain form made these epilogues a sixth of a short tile's time.)
+constexpr int kStageRow = 20;  // fp32 per staged row of 16 columns (padded: the
+                               // writes of the four row groups fall in distinct banks)
+constexpr int kStageRowH = 40; // fp16 per staged row of 32 h columns (padded likewise)
+template <int PHASE, int MS, bool STAGE>
+__device__ __forceinline__ void block_epilogue(const GemmParams& p, f32x4 (&acc)[MS][kNSub],
+                                               int64_t row0, int ctile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  if (PHASE == kGateUp) {
+    // h = silu(g) * u at the true scale (activations came scaled by 2^-kx),
+    // then one power-of-two scale per row of the tile, from the row's
+    // largest |h| over the tile's 256 columns
+    float rmax[MS][4];
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kx = lds_rexp[mi * 16 + 4 * lq + i];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float g = __builtin_ldexpf(acc[mi][s][i], kx);
+          const float u = __builtin_ldexpf(acc[mi][s + 2][i], kx);
+          acc[mi][s][i] = silu_mul(g, u);
+        }
+        rmax[mi][i] = max16(fmaxf(fabsf(acc[mi][0][i]), fabsf(acc[mi][1][i])));
+      }
+    if (lr == 0) {
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_rmax[wave][mi * 16 + 4 * lq + i] = rmax[mi][i];
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    if (tid < MS * 16) {
+      float m = lds_rmax[0][tid];
+#pragma unroll
+      for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, lds_rmax[w2][tid]);
+      const int kh = scale_exp(m);
+      lds_rkh[tid] = kh;
+      p.h_exp[(row0 + tid) * p.n_htiles + ctile] = kh;
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    _Float16* h16 = reinterpret_cast<_Float16*>(p.h_routed);
+    if (STAGE) {
+      // the wave's 32 h columns of each row, in the stored order
+      _Float16* st = reinterpret_cast<_Float16*>(lds_a0 + wave * 8192);
+      static_assert(kBM * kStageRowH * 2 <= 8192, "h staging area");
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int pc = perm_pos(16 * s + lr);
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = mi * 16 + 4 * lq + i;
+            st[r * kStageRowH + pc] = (_Float16)__builtin_ldexpf(acc[mi][s][i], -lds_rkh[r]);
+          }
+      }
+      const int col0 = ctile * (kBN / 2) + wave * 32;  // the wave's 32 columns lie all
+      if (col0 < p.I) {                                // inside the width or all past it
+        // piece q = 64 u + lane: row q / 4, 8 stored positions 8 (q % 4) ..
+#pragma unroll
+        for (int u = 0; u < MS; ++u) {
+          const int q = 64 * u + lane;
+          const int r = q >> 2, g = q & 3;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * kStageRowH + 8 * g);
+          *reinterpret_cast<u32x4*>(h16 + (row0 + r) * p.I + col0 + 8 * g) = v;
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int col = ctile * (kBN / 2) + wave * 32 + 16 * s + lr;
+      if (col >= p.I) continue;
+      const int pc = perm_pos(col);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mi * 16 + 4 * lq + i;
+          h16[(row0 + r) * p.I + pc] = (_Float16)__builtin_ldexpf(acc[mi][s][i], -lds_rkh[r]);
+        }
+    }
+  } else if (STAGE) {
+    // one 16-column sub-tile at a time: all rows of it through the wave's LDS
+    // area, then 16 bytes (4 columns of a row) per lane
+    float* st = reinterpret_cast<float*>(lds_a0 + wave * 8192);
+    static_assert(kBM * kStageRow * 4 <= 8192, "y staging area");
+    const int colw = ctile * kBN + wave * 64;  // the wave's 64 columns lie all inside
+    if (colw >= p.N) return;                   // the width or all past it
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) {
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mi * 16 + 4 * lq + i;
+          st[r * kStageRow + lr] = __builtin_ldexpf(acc[mi][s][i], lds_rexp[r]);
+        }
+      // piece q = 64 u + lane: row q / 4, columns 4 (q % 4) ..
+#pragma unroll
+      for (int u = 0; u < MS; ++u) {
+        const int q = 64 * u + lane;
+        const int r = q >> 2, g = q & 3;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(st + r * kStageRow + 4 * g);
+        const int32_t pair = lds_rpair[r];
+        if (pair < p.P)
+          *reinterpret_cast<f32x4*>(p.y_routed + (int64_t)pair * p.N + colw + 16 * s + 4 * g) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mi * 16 + 4 * lq + i;
+        const int64_t row = row0 + r;
+        const int32_t pair = p.sorted_ids[row];
+        if (pair >= p.P) continue;
+        const int kr = lds_rexp[r];
+        float* dst = p.y_routed + (int64_t)pair * p.N;
+#pragma unroll
+        for (int s = 0; s < kNSub; ++s) {
+          const int col = ctile * kBN + wave * 64 + 16 * s + lr;
+          if (col < p.N) dst[col] = __builtin_ldexpf(acc[mi][s][i], kr);
+        }
+      }
+  }
+}
+
 // ---- routed int4 blocks ---------------------------------------------------------
 // K advances in chunks of 128 inputs (four groups of 32). Each wave streams
 // its own 64 weight rows straight into registers: lane (lr, lq) loads group
@@ -379,29 +617,9 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
   const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
   const int64_t wbase = (int64_t)e * Nw;
 
-  // ---- activation copies: instruction u covers LDS rows 4u..4u+3 ------------
-  constexpr int kACopies = kBM / 4;
-  constexpr int kAPW = kACopies / kWaves;
-  static_assert(kACopies % kWaves == 0, "activation copies per wave");
-  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.a_routed, 0,
-      (int)((PHASE == kGateUp ? p.T : (int64_t)p.max_blocks * kBM) * K * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t ares = block_act_rsrc<PHASE>(p);
   uint32_t aoff[kAPW];
-#pragma unroll
-  for (int i = 0; i < kAPW; ++i) {
-    const int row = 4 * (kAPW * wave + i) + (lane >> 4);
-    const int piece = (lane & 15) ^ aslot(row & 15);
-    int64_t src = -1;
-    if (row < MS * 16) {
-      if (PHASE == kGateUp) {
-        const int32_t pair = p.sorted_ids[row0 + row];
-        if (pair < p.P) src = pair / p.k;
-      } else {
-        src = row0 + row;
-      }
-    }
-    aoff[i] = src < 0 ? kNoRow : (uint32_t)((src * K + piece * 8) * 2);
-  }
+  block_act_offsets<PHASE, MS>(p, row0, aoff);
   // slot c of tile t; past the tiles or the chunks, offsets past any buffer
   // (zeros; the copies are issued all the same, so that every chunk waits on
   // the same number of loads)
@@ -473,19 +691,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       *reinterpret_cast<u32x4*>(lds_sc[wave] + i * 1024 + lane * 16) = r[i];
   };
 
-  // per-row activation exponents for the epilogue (gate_up: the token's;
-  // down: the row's, after h_rescale_kernel), made visible by the first
-  // barrier
-  if (tid < kBM) {
-    int v = 0;
-    if (PHASE == kGateUp) {
-      const int32_t pair = p.sorted_ids[row0 + tid];
-      if (pair < p.P) v = p.a_exp[pair / p.k];
-    } else if (tid < MS * 16) {
-      v = p.a_exp[row0 + tid];
-    }
-    lds_rexp[tid] = v;
-  }
+  block_row_exps<PHASE, MS>(p, row0);  // made visible by the first barrier
 
   f32x4 acc[MS][kNSub];
 #pragma unroll
@@ -602,78 +808,6 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
     __builtin_amdgcn_s_barrier();
   };
 
-  // ---- epilogue: lane holds rows 4 lq + i of each 16-row sub-tile, column lr
-  auto epilogue = [&](int ctile) {
-    if (PHASE == kGateUp) {
-      // h = silu(g) * u at the true scale (activations came scaled by 2^-kx),
-      // then one power-of-two scale per row of the tile, from the row's
-      // largest |h| over the tile's 256 columns
-      float rmax[MS][4];
-#pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kx = lds_rexp[mi * 16 + 4 * lq + i];
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const float g = __builtin_ldexpf(acc[mi][s][i], kx);
-            const float u = __builtin_ldexpf(acc[mi][s + 2][i], kx);
-            acc[mi][s][i] = silu_mul(g, u);
-          }
-          rmax[mi][i] = max16(fmaxf(fabsf(acc[mi][0][i]), fabsf(acc[mi][1][i])));
-        }
-      if (lr == 0) {
-#pragma unroll
-        for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lds_rmax[wave][mi * 16 + 4 * lq + i] = rmax[mi][i];
-      }
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      if (tid < MS * 16) {
-        float m = lds_rmax[0][tid];
-#pragma unroll
-        for (int w2 = 1; w2 < kWaves; ++w2) m = fmaxf(m, lds_rmax[w2][tid]);
-        const int kh = scale_exp(m);
-        lds_rkh[tid] = kh;
-        p.h_exp[(row0 + tid) * p.n_htiles + ctile] = kh;
-      }
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      _Float16* h16 = reinterpret_cast<_Float16*>(p.h_routed);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int col = ctile * (kBN / 2) + wave * 32 + 16 * s + lr;
-        if (col >= p.I) continue;
-        const int pc = perm_pos(col);
-#pragma unroll
-        for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mi * 16 + 4 * lq + i;
-            h16[(row0 + r) * p.I + pc] = (_Float16)__builtin_ldexpf(acc[mi][s][i], -lds_rkh[r]);
-          }
-      }
-    } else {
-#pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = mi * 16 + 4 * lq + i;
-          const int64_t row = row0 + r;
-          const int32_t pair = p.sorted_ids[row];
-          if (pair >= p.P) continue;
-          const int kr = lds_rexp[r];
-          float* dst = p.y_routed + (int64_t)pair * p.N;
-#pragma unroll
-          for (int s = 0; s < kNSub; ++s) {
-            const int col = ctile * kBN + wave * 64 + 16 * s + lr;
-            if (col < p.N) dst[col] = __builtin_ldexpf(acc[mi][s][i], kr);
-          }
-        }
-    }
-  };
-
   // ---- pipeline -------------------------------------------------------------
   // slots 0, 1, 2 (and the first scale period) in flight, slot 0 landed
   u32x4 w0[kNSub], w1[kNSub], w2[kNSub], w3[kNSub];
@@ -699,13 +833,251 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       chunk(t, c + 2, 2, lds_a2, lds_a1, w2, w0, w1);
       chunk(t, c + 3, 3, lds_a3, lds_a2, w3, w0, w1);  // (no weight loads)
     }
-    epilogue(tile + t);
+    block_epilogue<PHASE, MS, false>(p, acc, row0, tile + t);
     if (!MT) break;
 #pragma unroll
     for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
       for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+}
+
+// ---- routed int4 blocks, weights through LDS ---------------------------------------
+// The checkpoint layout's weight rows are 4096 bytes apart, and a chunk takes
+// 64 bytes of each: loaded straight into MFMA registers (16 rows per load)
+// that is half of each 128-byte line per load, a load shape that runs at a
+// quarter of the whole-line rate, and the line's other half is often fetched
+// again a chunk later. This form stages the weights through LDS in stages of
+// 256 inputs, one whole 128-byte line per row: each wave copies its own 64
+// rows (8 copies of 8 rows x 128 bytes, LDS destination, the 16-byte piece
+// P ^ sswz(r) of row r into slot P as in the shared-expert tiles) into its
+// own 8 KB of lds_a0, and at the start of the stage reads its fragments
+// (lane (lr, lq) of sub-tile s: groups lq and lq + 4 of row 16 s + lr, 16
+// bytes each) into registers before it copies the next stage into the same
+// place; no other wave reads them, so they need no barrier. The stage's two
+// 128-input chunks run as before: chunk h takes group lq + 4 h of each lane,
+// MFMA step j word j of it. The activations take the three other LDS
+// buffers, a ring of three chunks (each copied two chunks ahead); the scales
+// of a stage (8 groups of each of the wave's rows, 16 bytes) are loaded into
+// registers one stage ahead, stored to the wave's LDS area with groups q and
+// q + 4 in word q, and read back at the stage's start. One barrier per chunk.
+template <int PHASE, int MS>
+__device__ __forceinline__ void block_tile_w(const GemmParams& p, int mblk, int tile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int K = p.K;
+  const int nch = K / kKC;        // 128-input chunks
+  const int nst = (nch + 1) / 2;  // 256-input weight stages (an odd chunk count
+                                  // leaves the last stage's second half unused)
+  const int64_t row0 = (int64_t)mblk * kBM;
+  const int e = p.block_expert[mblk];
+  const int Nw = (PHASE == kGateUp) ? 2 * p.I : p.N;
+  const int64_t wbase = (int64_t)e * Nw;
+
+  const __amdgpu_buffer_rsrc_t ares = block_act_rsrc<PHASE>(p);
+  uint32_t aoff[kAPW];
+  block_act_offsets<PHASE, MS>(p, row0, aoff);
+  // chunk c; past the chunks, offsets past any buffer (zeros; issued all the
+  // same, so that every chunk waits on the same number of loads)
+  auto copy_a = [&](uint8_t* dst, int c) {
+    const int so = uniform(c < nch ? c * kKC * 2 : (int)kNoRow);
+#pragma unroll
+    for (int i = 0; i < kAPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr)(dst + (kAPW * wave + i) * 1024), 16,
+                                               aoff[i], so, 0, 0);
+  };
+
+  // weights: copy i covers the wave's rows 8 i .. 8 i + 7 (lane / 8), lane
+  // % 8 the slot
+  constexpr int kWRow = 2 * kKC / 2;  // bytes of a row per stage: 128
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.packed + wbase * (K / 8)), 0, Nw * (K / 8) * 4, kBufferFlags);
+  // The weight row of the wave's row 8 i + r is n0 + 8 i + r, except that
+  // gate_up's rows 32..63 (the up sub-tiles) continue at I + n0: a lane
+  // offset (row r, its slot's piece; the swizzle of row 8 i + r is that of
+  // row 8 (i % 2) + r) and a uniform offset per copy. Widths are multiples of
+  // 128, so a wave's 64 rows are all inside the width or all past it.
+  const int n0 = weight_row<PHASE>(p, tile, wave * 64);
+  uint32_t wlane[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    wlane[i] = n0 < 0 ? kNoRow
+                      : (uint32_t)((n0 + (lane >> 3)) * (K / 2) + 16 * ((lane & 7) ^ sswz(r)));
+  }
+  const int wup = PHASE == kGateUp ? (p.I - 32) * (K / 2) : 0;
+  uint8_t* const wbuf = lds_a0 + wave * (64 * kWRow);
+  auto copy_w = [&](int st, int i) {  // copy i (rows 8 i ..) of stage st
+    const int so = uniform(st < nst ? st * kWRow + 8 * i * (K / 2) + (i >= 4 ? wup : 0) : (int)kNoRow);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr)(wbuf + i * 1024), 16, wlane[i & 1], so,
+                                             0, kWLdsAux);
+  };
+  // scales: lane l loads the 16 bytes (8 groups) of the wave's row l
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.scales + wbase * (K / 32)), 0, Nw * (K / 32) * 2, kBufferFlags);
+  const int nsc = weight_row<PHASE>(p, tile, wave * 64 + lane);
+  const uint32_t scoff = nsc < 0 ? kNoRow : (uint32_t)(nsc * (K / 16));
+  auto load_sc = [&](int st) {
+    const int so = uniform(st < nst ? st * 16 : (int)kNoRow);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres, scoff, so, 0));
+  };
+  uint8_t* const scbuf = lds_sc[wave];
+  auto store_sc = [&](const u32x4 v) {
+    // word q: groups q (low half) and q + 4 (high half)
+    const u32x4 o = {(v[0] & 0xFFFFu) | (v[2] << 16), (v[0] >> 16) | (v[2] & 0xFFFF0000u),
+                     (v[1] & 0xFFFFu) | (v[3] << 16), (v[1] >> 16) | (v[3] & 0xFFFF0000u)};
+    *reinterpret_cast<u32x4*>(scbuf + lane * 16) = o;
+  };
+
+  f32x4 acc[MS][kNSub];
+#pragma unroll
+  for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) acc[mi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int aread = lr * (kKC * 2);
+  const int wrd = lr * kWRow;
+  const int pw0 = 16 * ((0 + lq) ^ sswz(lr));  // sswz(16 s + lr) == sswz(lr)
+  const int pw1 = 16 * ((4 + lq) ^ sswz(lr));
+  u32x4 w[2][kNSub];     // the stage's weight fragments: [chunk][sub-tile]
+  uint32_t scr[kNSub];   // the stage's scales: groups lq, lq + 4 of each sub-tile row
+  u32x4 sreg;            // the next stage's scales, in flight
+  auto read_stage = [&]() {
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) {
+      w[0][s] = *reinterpret_cast<const u32x4*>(wbuf + s * 16 * kWRow + wrd + pw0);
+      w[1][s] = *reinterpret_cast<const u32x4*>(wbuf + s * 16 * kWRow + wrd + pw1);
+      scr[s] = *reinterpret_cast<const uint32_t*>(scbuf + (16 * s + lr) * 16 + 4 * lq);
+    }
+  };
+  // issue(j) runs before MFMA step j (the copies spread over the chunk)
+  auto compute = [&](const uint8_t* abuf, int h, auto&& issue) {
+    h16x2 sc[kNSub];
+#pragma unroll
+    for (int s = 0; s < kNSub; ++s) sc[s] = scale_pair(h ? scr[s] >> 16 : scr[s] & 0xFFFFu);
+    // activation fragments of step j: row 16 mi + lr, piece 4 lq + j; with
+    // kAPipe, step j + 1's are read before step j's MFMAs (two register sets)
+    h16x8 a[kAPipe ? 2 : 1][MS];
+    auto read_a = [&](h16x8 (&d)[MS], int j) {
+      const int apc = aread + (((4 * lq + j) ^ aslot(lr)) * 16);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+        d[mi] = *reinterpret_cast<const h16x8*>(abuf + mi * 16 * (kKC * 2) + apc);
+    };
+    if (kAPipe) read_a(a[0], 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // the two waves of a SIMD share its issue slots, and the older one
+      // wins ties: with one priority the younger one falls behind and the
+      // older one then idles at the chunk's barrier; a priority that drops
+      // with each step lets the wave that is behind catch up
+      if (kStepPrio) {
+        if (j == 0) __builtin_amdgcn_s_setprio(3);
+        else if (j == 1) __builtin_amdgcn_s_setprio(2);
+        else if (j == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+      issue(j);
+      __builtin_amdgcn_sched_barrier(0);
+      h16x8 (&cur)[MS] = a[kAPipe ? (j & 1) : 0];
+      const bool reads = !kAPipe || j < 3;
+      if (!kAPipe) read_a(a[0], j);
+      else if (j < 3) read_a(a[(j + 1) & 1], j + 1);
+#pragma unroll
+      for (int s = 0; s < kNSub; ++s) {
+        const h16x8 b = dequant8(w[h][s][j], sc[s]);
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi)
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mi], b, acc[mi][s], 0, 0, 0);
+      }
+      if (kWLdsSched == 1) {
+        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 13, 0);  // VALU: first sub-tile's weights
+#pragma unroll
+        for (int i = 0; i < MS * kNSub; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (kWLdsSched == 2) {
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Chunk c = 2 n + h of stage n, its activations in abuf, chunk c + 2's
+  // copied into anext (freed by the previous barrier). The copies are spread
+  // over the chunk's four MFMA steps: issued all at once, the eight waves'
+  // copies fill the compute unit's vector-memory queue and every wave stalls
+  // on issue while its MFMAs wait. Loads issued per chunk, in this order:
+  // before step 0 chunk c + 2's activations (kAPW); for h = 0 then the
+  // weights of stage n + 1, two copies before each step, and the scales of
+  // stage n + 1 (1) before step 3. Before the barrier, chunk c + 1's
+  // activations (and for h = 1 the next stage's weights and scales, issued
+  // after them in chunk c - 1) must have landed; the loads issued after them
+  // may stay in flight: h = 0: kAPW + 8 + 1 = 12; h = 1: kAPW = 3.
+  static_assert(kAPW == 3, "wait counts");
+  auto chunk = [&](int c, int h, const uint8_t* abuf, uint8_t* anext) {
+    const int n = c >> 1;
+    if (h == 0) {
+      read_stage();
+      wait_lgkm0();  // the fragments are in registers before the copies overwrite them
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto issue = [&](int j) {
+      if (j == 0) copy_a(anext, c + 2);
+      if (h == 0) {
+        copy_w(n + 1, 2 * j);
+        copy_w(n + 1, 2 * j + 1);
+        if (j == 3) sreg = load_sc(n + 1);
+      }
+    };
+    if (c < nch) {
+      compute(abuf, h, issue);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) issue(j);
+    }
+    if (h == 1) store_sc(sreg);  // after this stage's read_stage (a wave's LDS accesses are in order)
+    if (h == 0) wait_vm<12>();
+    else wait_vm<3>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+  };
+
+  block_row_exps<PHASE, MS, true>(p, row0);  // made visible by the first barrier
+  // stage 0's scales and weights, chunks 0 and 1's activations; chunk 0 and
+  // the weights landed before the first barrier
+  sreg = load_sc(0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) copy_w(0, i);
+  copy_a(lds_a1, 0);
+  copy_a(lds_a2, 1);
+  store_sc(sreg);
+  wait_vm<kAPW>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  // chunk c sits in buffer c % 3 (lds_a1, lds_a2, lds_a3)
+  for (int c = 0;; c += 6) {
+    // (already true here; stated so that the compiler's wait insertion, which
+    // merges the loop entry with the back edge, knows that only chunk c + 1's
+    // copies are in flight and adds no wait before chunk c's reads)
+    wait_vm<kAPW>();
+    chunk(c, 0, lds_a1, lds_a3);
+    chunk(c + 1, 1, lds_a2, lds_a1);
+    if (c + 2 >= nch) break;
+    chunk(c + 2, 0, lds_a3, lds_a2);
+    chunk(c + 3, 1, lds_a1, lds_a3);
+    if (c + 4 >= nch) break;
+    chunk(c + 4, 0, lds_a2, lds_a1);
+    chunk(c + 5, 1, lds_a3, lds_a2);
+    if (c + 6 >= nch) break;
+  }
+  wait_vm<0>();  // the copies past the last chunk (zeros) are done with LDS
+  block_epilogue<PHASE, MS, true>(p, acc, row0, tile);
 }
 
 // ---- shared-expert tiles (bf16 weights) -----------------------------------------
@@ -722,7 +1094,6 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
 // (into the other buffer) after the barrier, the wave's weight fragments,
 // then its weight copies of the next stage (they run under the activation
 // reads, the MFMAs and the next barrier), the activation fragments, the MFMAs.
-__device__ __forceinline__ int sswz(int r) { return (r >> 1) & 7; }
 
 template <int PHASE, int MS>
 __device__ __forceinline__ void shared_tile(const GemmParams& p, int64_t t0, int tile) {
@@ -886,6 +1257,15 @@ __device__ __forceinline__ void run_block(const GemmParams& p, int mblk, int til
     n_valid += __popcll(__ballot(r < kBM && p.sorted_ids[row0 + r] < p.P));
   }
   const int msub = uniform((n_valid + 15) >> 4);
+  if constexpr (kWeightsLds && !PK && !MT) {
+    if (kOddSubtiles && kMaxMS == 6 && msub == 3) block_tile_w<PHASE, 3>(p, mblk, tile);
+    else if (kOddSubtiles && kMaxMS == 6 && msub == 5) block_tile_w<PHASE, 5>(p, mblk, tile);
+    else if (msub <= 2) block_tile_w<PHASE, 2>(p, mblk, tile);
+    else if (msub <= 4 || kMaxMS < 6) block_tile_w<PHASE, (kMaxMS < 4 ? kMaxMS : 4)>(p, mblk, tile);
+    else if (msub <= 6 || kMaxMS < 8) block_tile_w<PHASE, (kMaxMS < 6 ? kMaxMS : 6)>(p, mblk, tile);
+    else block_tile_w<PHASE, kMaxMS>(p, mblk, tile);
+    return;
+  }
   if (kOddSubtiles && kMaxMS == 6 && (msub == 3 || msub == 5)) {
     if (msub == 3) block_tile<PHASE, 3, PK, MT>(p, mblk, tile, ntl);
     else block_tile<PHASE, 5, PK, MT>(p, mblk, tile, ntl);
