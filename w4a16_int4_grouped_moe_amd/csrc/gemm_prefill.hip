@@ -34,20 +34,26 @@
 // owns four 16-row weight sub-tiles (gate_up: two gate sub-tiles and the two
 // matching up sub-tiles) and computes them for all of the block's rows, so
 // each weight is dequantised exactly once per block. K advances in chunks of
-// 128 inputs (four 32-input groups); a chunk's operands are requested three
-// chunks before its MFMAs:
-//  * activations: a ring of four kBM x 128 chunks in LDS, copied straight
-//    from HBM (buffer loads with an LDS destination); a row's 16 pieces of 16
+// 128 inputs (four 32-input groups):
+//  * activations: a ring of kBM x 128 chunks in LDS, copied straight from
+//    HBM (buffer loads with an LDS destination); a row's 16 pieces of 16
 //    bytes are permuted, piece c of row r at slot c ^ f(r & 15) where f swaps
 //    the two 2-bit halves of its argument, so that the fragment reads (16 rows
 //    at one k offset per 16 lanes) are free of bank conflicts on gfx950
 //    16-byte LDS reads (the simpler XOR forms are not);
-//  * weights: no other wave reads a wave's weight rows, so they go straight
-//    to registers: lane (r = lane % 16, q = lane / 16) loads group q of row r
-//    of each of its four sub-tiles (16 bytes each), a ring of four chunks;
-//  * scales: per wave, 16 groups (four chunks) of each of its 64 rows, copied
-//    into LDS once per four chunks (two buffers that alternate), read into
-//    registers at the first chunk of each period;
+//  * weights, checkpoint layout, one tile per work-group (block_tile_w): each
+//    wave copies its own 64 rows into its own 8 KB of LDS in stages of 256
+//    inputs, one whole 128-byte line per row, and reads its fragments into
+//    registers at the start of the stage; the activation ring holds three
+//    chunks, each copied two chunks ahead; the copies of a chunk go out a few
+//    at a time between its MFMA steps;
+//  * weights, prepacked layout or several tiles per work-group (block_tile):
+//    lane (r = lane % 16, q = lane / 16) loads group q of row r of each of its
+//    four sub-tiles straight into registers (16 bytes each), a ring of four
+//    chunks; the activation ring holds four chunks, three ahead;
+//  * scales: per wave, the groups of its rows for a stage (or a period of four
+//    chunks), loaded into registers, stored to the wave's LDS area and read
+//    back at the start of the stage;
 //  * the words are dequantised to fp16 (u - 8) * s and fed to the MFMA: step j
 //    of a chunk takes word j of every lane, so its 32-long reduction covers one
 //    8-input slice of each of the four groups; the matching activations are
@@ -56,14 +62,13 @@
 // One barrier per chunk, which also frees the activation slot that the next
 // copies overwrite. Barriers are raw s_barrier with explicit waits (the fence
 // of __syncthreads() would also wait for the copies just issued). The number
-// of 16-row sub-tiles holding bucket rows (even, after rounding up) is a
-// template parameter of the K loop, so the loop body is straight-line code.
-// Widths that are not whole tiles (hidden % 512, inter % 256) run masked:
-// weight rows past the width read zeros and their outputs are not stored.
+// of 16-row sub-tiles holding bucket rows is a template parameter of the K
+// loop, so the loop body is straight-line code. Widths that are not whole
+// tiles (hidden % 512, inter % 256) run masked: weight rows past the width
+// read zeros and their outputs are not stored.
 //
-// Shared-expert work-group: 96 tokens x 512 weight rows, activations through
-// LDS as above (bf16, rows = tokens), each wave streams its own bf16 weight
-// rows into registers, three MFMA steps ahead.
+// Shared-expert work-group: 128 tokens x 512 weight rows of the bf16 weights,
+// both operands through LDS in stages of 64 inputs (see shared_tile).
 #include "internal.h"
 
 namespace moe {
@@ -150,12 +155,6 @@ constexpr bool kStepPrio = MOE_PREFILL_STEP_PRIO != 0;
 // instruction order of an MFMA step in that tile (as kPrefillSched); the
 // compiler's own order measured 2-3% faster there than the fixed interleave
 constexpr int kWLdsSched = MOE_PREFILL_WLDS_SCHED;
-#ifndef MOE_PREFILL_APIPE
-#define MOE_PREFILL_APIPE 0
-#endif
-// LDS-staged tile: the activation fragments of an MFMA step are read during
-// the previous step (two register sets)
-constexpr bool kAPipe = MOE_PREFILL_APIPE != 0;
 #ifndef MOE_SHARED_TOKENS
 #define MOE_SHARED_TOKENS 128
 #endif
@@ -958,16 +957,6 @@ __device__ __forceinline__ void block_tile_w(const GemmParams& p, int mblk, int 
     h16x2 sc[kNSub];
 #pragma unroll
     for (int s = 0; s < kNSub; ++s) sc[s] = scale_pair(h ? scr[s] >> 16 : scr[s] & 0xFFFFu);
-    // activation fragments of step j: row 16 mi + lr, piece 4 lq + j; with
-    // kAPipe, step j + 1's are read before step j's MFMAs (two register sets)
-    h16x8 a[kAPipe ? 2 : 1][MS];
-    auto read_a = [&](h16x8 (&d)[MS], int j) {
-      const int apc = aread + (((4 * lq + j) ^ aslot(lr)) * 16);
-#pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
-        d[mi] = *reinterpret_cast<const h16x8*>(abuf + mi * 16 * (kKC * 2) + apc);
-    };
-    if (kAPipe) read_a(a[0], 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // the two waves of a SIMD share its issue slots, and the older one
@@ -982,19 +971,21 @@ __device__ __forceinline__ void block_tile_w(const GemmParams& p, int mblk, int 
       }
       issue(j);
       __builtin_amdgcn_sched_barrier(0);
-      h16x8 (&cur)[MS] = a[kAPipe ? (j & 1) : 0];
-      const bool reads = !kAPipe || j < 3;
-      if (!kAPipe) read_a(a[0], j);
-      else if (j < 3) read_a(a[(j + 1) & 1], j + 1);
+      // activation fragments: row 16 mi + lr, piece 4 lq + j
+      h16x8 a[MS];
+      const int apc = aread + (((4 * lq + j) ^ aslot(lr)) * 16);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+        a[mi] = *reinterpret_cast<const h16x8*>(abuf + mi * 16 * (kKC * 2) + apc);
 #pragma unroll
       for (int s = 0; s < kNSub; ++s) {
         const h16x8 b = dequant8(w[h][s][j], sc[s]);
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi)
-          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[mi], b, acc[mi][s], 0, 0, 0);
+          acc[mi][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], b, acc[mi][s], 0, 0, 0);
       }
       if (kWLdsSched == 1) {
-        if (reads) __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x002, 13, 0);  // VALU: first sub-tile's weights
 #pragma unroll
         for (int i = 0; i < MS * kNSub; ++i) {
