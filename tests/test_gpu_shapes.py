@@ -43,6 +43,7 @@ CASES = [
     (301, 1024, 768, 4, 3, 0, False, 96),  # no shared expert, 308k outputs
     (1100, 1024, 768, 4, 3, 0, False, 96), # no shared expert, 1.13M outputs
     (260, 896, 1152, 5, 2, 0, False, 96),  # no shared expert, masked tiles, 7 / 9 chunks
+    (200, 512, 128, 4, 2, 0, True, 96),    # down K = 128: a single chunk; gate_up tile half masked
 ]
 
 
