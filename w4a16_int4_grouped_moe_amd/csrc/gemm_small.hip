@@ -164,7 +164,11 @@ __device__ __forceinline__ float kpart_sum(float v) {
 // Output columns per wave slice: gate_up slices cover 2*NR h columns (NR/2
 // gate + NR/2 up row-sets), down slices cover 4*NR output columns.
 template <int PHASE, int NR>
-constexpr int slice_cols() { return PHASE == kGateUp ? 2 * NR : 4 * NR; }
+constexpr int slice_cols() {
+  static_assert(PHASE != kGateUp || NR % 2 == 0,
+                "a gate_up slice pairs NR / 2 gate row-sets with NR / 2 up row-sets");
+  return PHASE == kGateUp ? 2 * NR : 4 * NR;
+}
 
 // weight row of row-set rs, row j, of wave slice `slice`
 template <int PHASE, int NR>
@@ -1314,7 +1318,15 @@ hipError_t launch_small(const GemmParams& p, hipStream_t stream) {
 // Streamed down launch. Slice groups per routed work-group: enough routed
 // work-groups to hold about kStreamTargetWG of them (the bucket count is not
 // known on the host; min(pairs, experts) estimates it), at most kStreamSG.
-constexpr int64_t kStreamTargetWG = 2048;
+#ifndef MOE_STREAM_TARGET_WG
+#define MOE_STREAM_TARGET_WG 2048
+#endif
+constexpr int64_t kStreamTargetWG = MOE_STREAM_TARGET_WG;
+#ifndef MOE_STREAM_ONE_ROUND
+#define MOE_STREAM_ONE_ROUND 1
+#endif
+constexpr bool kStreamOneRound = MOE_STREAM_ONE_ROUND != 0;
+constexpr int64_t kCUs = 256;  // MI355X compute units
 
 template <int NR, int NRS, int TB>
 hipError_t launch_stream_down(const GemmParams& p, hipStream_t stream) {
@@ -1328,10 +1340,23 @@ hipError_t launch_stream_down(const GemmParams& p, hipStream_t stream) {
   const int64_t est_blocks = std::max<int64_t>(1, std::min<int64_t>(p.P, p.max_blocks));
   int sgs = (int)std::min<int64_t>(kStreamSG, est_blocks * groups / kStreamTargetWG);
   if (sgs < 1) sgs = 1;
-  const int64_t routed = (int64_t)p.max_blocks * ((groups + sgs - 1) / sgs);
   const int64_t shared = p.wshared ? (p.T + 4 * TB - 1) / (4 * TB) *
                                          (p.N / slice_cols<kDown, NRS>() / kWaves)
                                    : 0;
+  if (kStreamOneRound) {
+    // a grid a little over one round of resident work-groups ends with a
+    // second round of a few work-groups that start late: take more slice
+    // groups per work-group where that fits the grid in one round
+    const int64_t slots = (int64_t)kCUs * 4 * waves_per_simd(NR) / kWaves;
+    auto grid_of = [&](int g) { return est_blocks * ((groups + g - 1) / g) + shared; };
+    if (grid_of(sgs) > slots)
+      for (int g = sgs + 1; g <= kStreamSG; ++g)
+        if (grid_of(g) <= slots) {
+          sgs = g;
+          break;
+        }
+  }
+  const int64_t routed = (int64_t)p.max_blocks * ((groups + sgs - 1) / sgs);
   const int64_t grid = routed + shared;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
