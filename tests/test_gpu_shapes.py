@@ -151,3 +151,46 @@ def test_split_buckets(dev, shared):
     ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
                          bank.scales_w2, sw, base)
     check(mi.bf16_tensor_to_f64(out), ref, f"split buckets shared={shared}")
+
+
+def _random_cases(seed, n):
+    """Seeded random shapes of the 96-row path: widths any multiple of 128 up
+    to 3968 (an odd or even number of 128-input chunks, masked column
+    tiles), 1-16 local experts with an expert base, top-1..8, with and
+    without a shared expert, enough pairs per expert for 96-row buckets (and
+    the split bucketing wherever an expert has at most 4 pairs)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = 128 * int(rng.integers(1, 32))
+        I = 128 * int(rng.integers(1, 17))
+        E = int(rng.integers(1, 17))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        base = int(rng.integers(0, 3))
+        T = int(rng.integers(4 * E // k + 8, 4 * E // k + 1200))
+        out.append((T, H, I, E, k, base, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("T,H,I,E,k,base,shared", _random_cases(2026, 12))
+def test_random_shapes_96(dev, T, H, I, E, k, base, shared):
+    import torch
+    import w4a16_int4_grouped_moe_amd as moe
+
+    assert moe.forward_block_m(moe.problem(T, H, I, E, k, base)) == 96
+    seed = 7000 + T + H + I
+    bank = mi.weight_bank(seed, H, I, list(range(base, base + E)))
+    bank_dev = {kk: mi.to_device(v, dev) for kk, v in bank.__dict__.items()}
+    x = mi.activations(seed + 1, T, H)
+    n_global = base + E + 2
+    ids, w = mi.routing_uniform(seed + 2, T, n_global, min(k, n_global))
+    if base:
+        ids[::7, 0] = -1
+    sw = mi.shared_weights(seed + 3, H, I) if shared else None
+    print(f"[case] random T={T} H={H} I={I} E={E} k={k} base={base} shared={shared}", flush=True)
+    out = run_layer(dev, x, ids, w, bank_dev, sw, expert_base=base)
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, ids, w, bank.packed_w13, bank.scales_w13, bank.packed_w2,
+                         bank.scales_w2, sw, base)
+    res = check(mi.bf16_tensor_to_f64(out), ref, f"random T={T} H={H} I={I} E={E} k={k}")
+    assert res["max_small_err_over_rms"] <= 0.015, res
