@@ -25,8 +25,9 @@ expert), timed in two legs:
 Secondary outputs: p10/p90 of the per-call times next to the median, warm
 back-to-back calls on one weight copy and replays of a call captured in a HIP
 graph (`per_batch`), and `achievable`: what this GPU reaches on a 1 GiB
-device copy and a bf16 library GEMM (measurement denominators only), with
-each roofline's `frac_of_achievable`.
+device copy and sum, a plain streaming-read kernel (libmoe_probe.so) and a
+bf16 library GEMM (measurement denominators only), with each roofline's
+`frac_of_achievable`.
 
 Inputs are seeded synthetic data, resident in HBM before timing starts. Launch
 durations come from HIP events that the library records around the launch on
@@ -390,10 +391,47 @@ def per_batch(leg, call_ms, st, gu_diag, dn_diag, gu_timed, route_us=None, warm_
     return out
 
 
+def stream_read_gbs(dev):
+    """HBM read rate of a plain streaming-read kernel (libmoe_probe.so, built
+    beside the library: 16 loads of 16 bytes in flight per lane,
+    non-temporal) over a 4 GiB buffer; measurement only."""
+    import ctypes
+    import torch
+
+    path = os.path.join(ROOT, "w4a16_int4_grouped_moe_amd", "libmoe_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.moe_probe_stream_read_bytes.argtypes = [ctypes.c_int64]
+    lib.moe_probe_stream_read_bytes.restype = ctypes.c_int64
+    n = 4 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def one():
+        rc = lib.moe_probe_stream_read(src.data_ptr(), n, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"stream-read probe: HIP error {rc}")
+
+    for _ in range(3):
+        one()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    gbs = lib.moe_probe_stream_read_bytes(n) * 10 / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, sink
+    return gbs
+
+
 def achievable(dev):
     """Secondary denominators measured on this GPU: a 1 GiB device copy (read +
-    write), a 1 GiB sum (read), and a bf16 8192^3 library GEMM (measurement
-    only; no part of the layer uses it)."""
+    write), a 1 GiB sum (read), a hand-written streaming read of 4 GiB, and a
+    bf16 8192^3 library GEMM (measurement only; no part of the layer uses
+    them)."""
     import torch
 
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -418,7 +456,8 @@ def achievable(dev):
     torch.cuda.synchronize()
     read_gbs = (1 << 30) * 10 / (a.elapsed_time(b) / 1e3) / 1e9
     del src, t
-    gbs = max(copy_gbs, read_gbs)
+    stream_gbs = stream_read_gbs(dev)
+    gbs = max(copy_gbs, read_gbs, stream_gbs)
     n = 8192
     x = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
     y = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
@@ -433,10 +472,13 @@ def achievable(dev):
     del x, y, z
     torch.cuda.empty_cache()
     return {"hbm_gbs": round(gbs, 1), "copy_gbs": round(copy_gbs, 1),
-            "read_gbs": round(read_gbs, 1), "bf16_tflops": round(tfs, 1),
-            "method": "HBM: the better of a 1 GiB device copy (bytes read + written) and a "
-                      "1 GiB sum (bytes read); MFMA: bf16 8192x8192x8192 matmul (library "
-                      "GEMM, measurement only)"}
+            "read_gbs": round(read_gbs, 1), "stream_read_gbs": round(stream_gbs, 1),
+            "bf16_tflops": round(tfs, 1),
+            "method": "HBM: the best of a 1 GiB device copy (bytes read + written), a "
+                      "1 GiB sum (bytes read) and a streaming-read kernel over 4 GiB "
+                      "(libmoe_probe.so: 16 loads of 16 bytes in flight per lane, "
+                      "non-temporal); MFMA: bf16 8192x8192x8192 matmul (library GEMM); "
+                      "measurement only"}
 
 
 def router_times(leg, dev, n):

@@ -46,6 +46,23 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(raw, name), name
 
 
+def test_probe_library_exports_its_entry_points():
+    """The bench's streaming-read kernel lives in its own library (measurement
+    only): it loads and exports its two calls; the pass size is whole grid
+    steps of 512 MiB."""
+    import os
+
+    raw = ctypes.CDLL(os.path.join(os.path.dirname(moe.LIB_PATH), "libmoe_probe.so"))
+    assert hasattr(raw, "moe_probe_stream_read")
+    raw.moe_probe_stream_read_bytes.argtypes = [ctypes.c_int64]
+    raw.moe_probe_stream_read_bytes.restype = ctypes.c_int64
+    assert raw.moe_probe_stream_read_bytes(4 << 30) == 4 << 30
+    assert raw.moe_probe_stream_read_bytes((1 << 29) - 1) == 0
+    raw.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    assert raw.moe_probe_stream_read(None, 1 << 30, None, None) != 0  # refused before any launch
+
+
 def test_status_codes_match_header(lib):
     text = open(HEADER).read()
     for name in ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_ALIGNMENT",
