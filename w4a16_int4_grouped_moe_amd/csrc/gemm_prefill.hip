@@ -13,8 +13,9 @@
 // Numerics: the int4 weights are exact. A code u of a group with scale s
 // (Kimi-K2.6 catalog entry, QUANT paragraph: symmetric, group 32) is the value
 // (u - 8) * s; with s a bf16 (8 significant bits) and |u - 8| <= 8 the product
-// has at most 11 significant bits, which is exactly an fp16 whenever
-// 2^-17 <= |s| <= 8188. So the routed products run on v_mfma_f32_16x16x32_f16:
+// has at most 11 significant bits, which is exactly an fp16; the kernel's
+// single-fma dequantisation (dequant8) gets it exactly for
+// 2^-17 <= |s| <= 2720. So the routed products run on v_mfma_f32_16x16x32_f16:
 //  * activations x are converted once per call to fp16 with one power-of-two
 //    scale per token (x16_kernel: the largest |x| of the token lands in
 //    [2^14, 2^15)), which is exact for every value down to 2^-32 of the
@@ -215,28 +216,63 @@ __device__ __forceinline__ h16x2 scale_pair(uint32_t bits) {
   return h16x2{h, h};
 }
 
+#ifndef MOE_DEQUANT_FMA
+#define MOE_DEQUANT_FMA 1
+#endif
+// 1: the single-fma dequantisation below (12 VALU per word); 0: subtract,
+// then multiply (13)
+constexpr bool kDequantFma = MOE_DEQUANT_FMA != 0;
+
+// A group's scale s as an fp16 pair and the pair -24 s (the offset of the
+// single-fma form below; exact for |s| <= 2720, i.e. 24 |s| <= 65504).
+struct GroupScale {
+  h16x2 s, c;
+};
+__device__ __forceinline__ GroupScale group_scale(uint32_t bits) {
+  const h16x2 s = scale_pair(bits);
+  const h16x2 m24 = {(_Float16)-24.0f, (_Float16)-24.0f};
+  return {s, s * m24};
+}
+
 // The eight codes of one word -> eight fp16 weights (u - 8) * s, in the order
 // of fields 0, 4, 1, 5, 2, 6, 3, 7 (activations are stored in the same order).
-// A field in bits 0-3 of a 16-bit half OR-ed into the fp16 pattern 0x6400 is
-// exactly 1024 + u, a field in bits 4-7 gives 1024 + 16 u: the word's low
-// byte pair (fields 0, 4 and 1, 5) needs no shift, its high byte pair (fields
-// 2, 6 and 3, 7) one shift by 8. (1024 + u) - 1032 and (1024 + 16 u) / 16 - 72
-// are exactly u - 8, and (u - 8) * s is exact in fp16 (at most 11 significant
-// bits). 13 VALU instructions per word (one shift, four v_bitop3, four packed
-// fp16 add/fma, four packed fp16 multiplies).
-__device__ __forceinline__ h16x8 dequant8(uint32_t w, h16x2 s2) {
-  const uint32_t w8 = w >> 8;
-  const h16x2 c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const h16x2 c16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const h16x2 c72 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const h16x2 h0 = __builtin_bit_cast(h16x2, and_or(w, 0x000F000Fu, 0x64006400u));   // u0, u4
-  const h16x2 h1 = __builtin_bit_cast(h16x2, and_or(w, 0x00F000F0u, 0x64006400u));   // u1, u5
-  const h16x2 h2 = __builtin_bit_cast(h16x2, and_or(w8, 0x000F000Fu, 0x64006400u));  // u2, u6
-  const h16x2 h3 = __builtin_bit_cast(h16x2, and_or(w8, 0x00F000F0u, 0x64006400u));  // u3, u7
-  const h16x2 q0 = (h0 + c1032) * s2;
-  const h16x2 q1 = __builtin_elementwise_fma(h1, c16, c72) * s2;
-  const h16x2 q2 = (h2 + c1032) * s2;
-  const h16x2 q3 = __builtin_elementwise_fma(h3, c16, c72) * s2;
+// Single-fma form: each field is shifted to bits 6-9 of its 16-bit half, right
+// below the implicit bit, and OR-ed into the fp16 pattern 0x4C00 (16.0): the
+// value is exactly 16 + u. fma(16 + u, s, -24 s) is (u - 8) * s before its
+// one rounding, and that product is exact in fp16 (at most 11 significant
+// bits), so the weight is exact whenever -24 s is: 2^-17 <= |s| <= 2720.
+// 12 VALU instructions per word (four shifts, four v_bitop3, four packed
+// fp16 fma). Two-step form: a field in bits 0-3 of a half OR-ed into 0x6400
+// is 1024 + u, one in bits 4-7 gives 1024 + 16 u; (1024 + u) - 1032 and
+// (1024 + 16 u) / 16 - 72 are exactly u - 8, then times s (exact for
+// 2^-17 <= |s| < 2^13); 13 instructions (one shift, four v_bitop3, four
+// packed add/fma, four packed multiplies).
+__device__ __forceinline__ h16x8 dequant8(uint32_t w, const GroupScale& g) {
+  h16x2 q0, q1, q2, q3;
+  if (kDequantFma) {
+    constexpr uint32_t kField = 0x03C003C0u, k16 = 0x4C004C00u;
+    q0 = __builtin_elementwise_fma(__builtin_bit_cast(h16x2, and_or(w << 6, kField, k16)), g.s,
+                                   g.c);  // u0, u4
+    q1 = __builtin_elementwise_fma(__builtin_bit_cast(h16x2, and_or(w << 2, kField, k16)), g.s,
+                                   g.c);  // u1, u5
+    q2 = __builtin_elementwise_fma(__builtin_bit_cast(h16x2, and_or(w >> 2, kField, k16)), g.s,
+                                   g.c);  // u2, u6
+    q3 = __builtin_elementwise_fma(__builtin_bit_cast(h16x2, and_or(w >> 6, kField, k16)), g.s,
+                                   g.c);  // u3, u7
+  } else {
+    const uint32_t w8 = w >> 8;
+    const h16x2 c1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const h16x2 c16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h16x2 c72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const h16x2 h0 = __builtin_bit_cast(h16x2, and_or(w, 0x000F000Fu, 0x64006400u));   // u0, u4
+    const h16x2 h1 = __builtin_bit_cast(h16x2, and_or(w, 0x00F000F0u, 0x64006400u));   // u1, u5
+    const h16x2 h2 = __builtin_bit_cast(h16x2, and_or(w8, 0x000F000Fu, 0x64006400u));  // u2, u6
+    const h16x2 h3 = __builtin_bit_cast(h16x2, and_or(w8, 0x00F000F0u, 0x64006400u));  // u3, u7
+    q0 = (h0 + c1032) * g.s;
+    q1 = __builtin_elementwise_fma(h1, c16, c72) * g.s;
+    q2 = (h2 + c1032) * g.s;
+    q3 = __builtin_elementwise_fma(h3, c16, c72) * g.s;
+  }
   return h16x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
 }
 
@@ -717,10 +753,10 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       }
   };
   auto compute = [&](const uint8_t* abuf, const u32x4 (&w)[kNSub], int q) {
-    h16x2 sc[kNSub];
+    GroupScale sc[kNSub];
 #pragma unroll
     for (int s = 0; s < kNSub; ++s)
-      sc[s] = scale_pair((q & 1) ? scr[s][q / 2] >> 16 : scr[s][q / 2] & 0xFFFFu);
+      sc[s] = group_scale((q & 1) ? scr[s][q / 2] >> 16 : scr[s][q / 2] & 0xFFFFu);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       h16x8 a[MS];
@@ -739,7 +775,7 @@ __device__ __forceinline__ void block_tile(const GemmParams& p, int mblk, int ti
       }
       if (kPrefillSched == 1) {
         __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 13, 0);  // VALU: first sub-tile's weights
+        __builtin_amdgcn_sched_group_barrier(0x002, kDequantFma ? 12 : 13, 0);  // VALU: first sub-tile's weights
 #pragma unroll
         for (int i = 0; i < MS * kNSub; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -954,9 +990,9 @@ __device__ __forceinline__ void block_tile_w(const GemmParams& p, int mblk, int 
   };
   // issue(j) runs before MFMA step j (the copies spread over the chunk)
   auto compute = [&](const uint8_t* abuf, int h, auto&& issue) {
-    h16x2 sc[kNSub];
+    GroupScale sc[kNSub];
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) sc[s] = scale_pair(h ? scr[s] >> 16 : scr[s] & 0xFFFFu);
+    for (int s = 0; s < kNSub; ++s) sc[s] = group_scale(h ? scr[s] >> 16 : scr[s] & 0xFFFFu);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // the two waves of a SIMD share its issue slots, and the older one
@@ -986,7 +1022,7 @@ __device__ __forceinline__ void block_tile_w(const GemmParams& p, int mblk, int 
       }
       if (kWLdsSched == 1) {
         __builtin_amdgcn_sched_group_barrier(0x100, MS, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 13, 0);  // VALU: first sub-tile's weights
+        __builtin_amdgcn_sched_group_barrier(0x002, kDequantFma ? 12 : 13, 0);  // VALU: first sub-tile's weights
 #pragma unroll
         for (int i = 0; i < MS * kNSub; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
