@@ -132,6 +132,12 @@ constexpr uint32_t kNoRow = 0x80000000u;   // offset past any buffer: loads 0
 // blocks of 33-48 and 65-80 rows run the K loop for 3 and 5 sub-tiles
 // (otherwise 4 and 6)
 constexpr bool kOddSubtiles = MOE_PREFILL_ODD_SUBTILES != 0;
+#ifndef MOE_PREFILL_ONE_SUBTILE
+#define MOE_PREFILL_ONE_SUBTILE 1
+#endif
+// blocks of at most 16 rows (an expert's last rows, the few-pair experts of
+// skewed batches) run the K loop for one sub-tile (otherwise two)
+constexpr bool kOneSubtile = MOE_PREFILL_ONE_SUBTILE != 0;
 #ifndef MOE_PREFILL_WLDS
 #define MOE_PREFILL_WLDS 1
 #endif
@@ -316,9 +322,7 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 template <int PHASE>
 constexpr int tile_cols() { return PHASE == kGateUp ? kBN / 2 : kBN; }
 
-// Permutations of 16-byte pieces in LDS: the four groups of weight row R, the
-// sixteen pieces of activation row r.
-__device__ __forceinline__ int wslot(int R) { return (R >> 1) & 3; }
+// Permutation of the sixteen 16-byte pieces of activation row r in LDS.
 __device__ __forceinline__ int aslot(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 // Permutation of the 16-byte pieces of a 128-byte row staged in LDS (the
 // shared-expert operands, the routed weights of the LDS-staged tile): piece
@@ -1287,6 +1291,7 @@ __device__ __forceinline__ void run_block(const GemmParams& p, int mblk, int til
   if constexpr (kWeightsLds && !PK && !MT) {
     if (kOddSubtiles && kMaxMS == 6 && msub == 3) block_tile_w<PHASE, 3>(p, mblk, tile);
     else if (kOddSubtiles && kMaxMS == 6 && msub == 5) block_tile_w<PHASE, 5>(p, mblk, tile);
+    else if (kOneSubtile && msub <= 1) block_tile_w<PHASE, 1>(p, mblk, tile);
     else if (msub <= 2) block_tile_w<PHASE, 2>(p, mblk, tile);
     else if (msub <= 4 || kMaxMS < 6) block_tile_w<PHASE, (kMaxMS < 4 ? kMaxMS : 4)>(p, mblk, tile);
     else if (msub <= 6 || kMaxMS < 8) block_tile_w<PHASE, (kMaxMS < 6 ? kMaxMS : 6)>(p, mblk, tile);
@@ -1298,7 +1303,8 @@ __device__ __forceinline__ void run_block(const GemmParams& p, int mblk, int til
     else block_tile<PHASE, 5, PK, MT>(p, mblk, tile, ntl);
     return;
   }
-  if (msub <= 2) block_tile<PHASE, 2, PK, MT>(p, mblk, tile, ntl);
+  if (kOneSubtile && msub <= 1) block_tile<PHASE, 1, PK, MT>(p, mblk, tile, ntl);
+  else if (msub <= 2) block_tile<PHASE, 2, PK, MT>(p, mblk, tile, ntl);
   else if (msub <= 4 || kMaxMS < 6) block_tile<PHASE, (kMaxMS < 4 ? kMaxMS : 4), PK, MT>(p, mblk, tile, ntl);
   else if (msub <= 6 || kMaxMS < 8) block_tile<PHASE, (kMaxMS < 6 ? kMaxMS : 6), PK, MT>(p, mblk, tile, ntl);
   else block_tile<PHASE, kMaxMS, PK, MT>(p, mblk, tile, ntl);
