@@ -168,9 +168,9 @@ int moe_w4a16_align_scratch_size(const moe_w4a16_problem *p, size_t *bytes);
  * after them, with h rounded to bf16. Larger calls (block_m 96) run the
  * routed products in fp16 (except experts with at most 4 pairs in a call of
  * fewer than 8192 pairs, which take the decode-sized path), where (u - 8) * s
- * is exact for bf16 group scales
- * with 2^-17 <= |s| <= 2720 (smaller ones round to fp16's subnormal grid,
- * larger ones overflow the fp16 offset -24 s of the dequantisation): x is converted once to fp16 with one power-of-two
+ * is exact for bf16 group scales with 2^-17 <= |s| <= 2720 (smaller ones
+ * round to fp16's subnormal grid, larger ones overflow the fp16 offset -24 s
+ * of the dequantisation): x is converted once to fp16 with one power-of-two
  * scale per token (exact down to 2^-32 of the token's largest |x|), and h is
  * rounded once to fp16 with one power-of-two scale per row and 256 columns.
  * The bf16 shared expert uses bf16 products with its h rounded to bf16.
