@@ -102,6 +102,12 @@ def test_workspace_size_and_block_m(lib):
     # take the same 96-row blocks, masked
     assert moe.forward_block_m(P(num_tokens=512, hidden=7040)) == 96
     assert moe.forward_block_m(P(num_tokens=4096, hidden=7040, inter=1152)) == 96
+    # the 4-row kernel stages a work-group's group scales for the whole K in
+    # its 64 KB of LDS (64 rows x 32 (odd number of 16-group units) bytes, plus
+    # two 4 KB activation stages): hidden 12288 fits (58 KB), 14336 does not
+    # (66 KB), and even one token then takes the 96-row blocks
+    assert moe.forward_block_m(P(num_tokens=1, hidden=12288)) == 4
+    assert moe.forward_block_m(P(num_tokens=1, hidden=14336)) == 96
     # one GPU's share of an 8-way tensor-parallel split (intermediate 256)
     assert moe.forward_block_m(P(inter=256)) == 4
     assert moe.forward_block_m(P(inter=256, num_tokens=4096)) == 96
