@@ -44,6 +44,8 @@ CASES = [
     (1100, 1024, 768, 4, 3, 0, False, 96), # no shared expert, 1.13M outputs
     (260, 896, 1152, 5, 2, 0, False, 96),  # no shared expert, masked tiles, 7 / 9 chunks
     (200, 512, 128, 4, 2, 0, True, 96),    # down K = 128: a single chunk; gate_up tile half masked
+    (2, 14336, 256, 8, 4, 0, True, 96),    # two tokens on 96-row blocks: the 4-row kernel's staged
+                                           # scales for K = 14336 exceed its LDS; one-row blocks
 ]
 
 
